@@ -11,9 +11,12 @@ __all__ = [
     "gemm_nt_f16",
     "gemm_nt_f16_ex",
     "gemm_nt_f16_config_name",
+    "gemm_nt_f16_select",
     "gemm_nt_f16_version",
     "variants",
     "library_path",
+    "load",
+    "GemmError",
 ]
 
 

@@ -1,0 +1,129 @@
+"""The C ABI library without a GPU: it loads, exports what the header
+declares, and rejects bad arguments on the host before enqueuing anything."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from dense_fp16_gemm_04_amd import binding, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_nt_f16.h")
+
+INVALID = 1  # hipErrorInvalidValue
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_nt_f16\w*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "gemm_nt_f16" in names and "gemm_nt_f16_ex" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding wraps exactly those
+    assert sorted(binding.SIGNATURES) == names
+
+
+def test_version_matches_header(lib):
+    m = re.search(r"#define\s+GEMM_NT_F16_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.gemm_nt_f16_version() == int(m.group(1))
+
+
+def test_variant_table(lib):
+    n = lib.gemm_nt_f16_variant_count()
+    assert n >= 2
+    names = [lib.gemm_nt_f16_variant_name(i) for i in range(n)]
+    assert all(isinstance(x, bytes) and x for x in names)
+    assert len(set(names)) == n
+    assert lib.gemm_nt_f16_variant_name(n) is None
+    assert lib.gemm_nt_f16_variant_name(-1) is None
+
+
+def test_selection(lib):
+    n = lib.gemm_nt_f16_variant_count()
+    for w in workloads.WORKLOADS:
+        v = lib.gemm_nt_f16_select(w.M, w.N, w.K)
+        assert 0 <= v < n
+        assert binding.gemm_nt_f16_config_name(w.M, w.N, w.K).startswith("mfma")
+    # K not a multiple of 8 cannot use the MFMA kernels
+    assert binding.gemm_nt_f16_config_name(64, 64, 7).startswith("simple")
+    assert lib.gemm_nt_f16_select(-1, 4, 4) == -1
+    assert lib.gemm_nt_f16_config_name(4, -4, 4) is None
+
+
+FAKE_A = 0x10000
+FAKE_B = 0x200000
+FAKE_C = 0x4000000
+
+
+def call(lib, a, b, c, M, N, K, variant=None):
+    if variant is None:
+        return lib.gemm_nt_f16(a, b, c, M, N, K, None)
+    return lib.gemm_nt_f16_ex(a, b, c, M, N, K, variant, None)
+
+
+def test_negative_dimensions_rejected(lib):
+    for M, N, K in [(-1, 4, 4), (4, -1, 4), (4, 4, -1)]:
+        assert call(lib, FAKE_A, FAKE_B, FAKE_C, M, N, K) == INVALID
+
+
+def test_null_pointers_rejected(lib):
+    assert call(lib, None, FAKE_B, FAKE_C, 4, 4, 4) == INVALID
+    assert call(lib, FAKE_A, None, FAKE_C, 4, 4, 4) == INVALID
+    assert call(lib, FAKE_A, FAKE_B, None, 4, 4, 4) == INVALID
+
+
+def test_empty_output_is_a_no_op(lib):
+    # nothing to write: success without touching any pointer or the GPU
+    assert call(lib, None, None, None, 0, 5, 5) == 0
+    assert call(lib, None, None, None, 5, 0, 5) == 0
+
+
+def test_overlap_rejected(lib):
+    # C [4 x 4] fp16 = 32 bytes starting inside A or B
+    assert call(lib, FAKE_A, FAKE_B, FAKE_A + 16, 4, 4, 8) == INVALID
+    assert call(lib, FAKE_A, FAKE_B, FAKE_B + 8, 4, 4, 8) == INVALID
+    assert call(lib, FAKE_A, FAKE_B, FAKE_A - 16, 4, 4, 8) == INVALID
+
+
+def test_odd_pointer_rejected(lib):
+    assert call(lib, FAKE_A + 1, FAKE_B, FAKE_C, 4, 4, 8) == INVALID
+
+
+def test_too_large_rejected(lib):
+    assert call(lib, FAKE_A, FAKE_B, FAKE_C, 1 << 31, 4, 8) == INVALID
+
+
+def test_variant_checks(lib):
+    n = lib.gemm_nt_f16_variant_count()
+    assert call(lib, FAKE_A, FAKE_B, FAKE_C, 4, 4, 8, variant=n) == INVALID
+    # an MFMA variant needs 16-byte aligned A and B and K % 8 == 0
+    assert call(lib, FAKE_A + 2, FAKE_B, FAKE_C, 4, 4, 8, variant=0) == INVALID
+    assert call(lib, FAKE_A, FAKE_B, FAKE_C, 4, 4, 6, variant=0) == INVALID
+
+
+def test_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros((4, 8), dtype=torch.float16)
+    b = torch.zeros((4, 8), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        binding.gemm_nt_f16(a, b)
+    with pytest.raises(ValueError):
+        binding.gemm_nt_f16(a, torch.zeros((4, 9), dtype=torch.float16))
+    with pytest.raises(ValueError):  # CPU tensors: no GPU path here
+        binding.gemm_nt_f16(a, torch.zeros((4, 8), dtype=torch.float16))
