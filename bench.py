@@ -77,7 +77,7 @@ def main(argv=None) -> int:
     p.add_argument("--workload", default="square_8192")
     p.add_argument("--variant", type=int, default=-1, help="kernel variant index (-1: automatic)")
     p.add_argument("--cooldown", type=float, default=3.0, help="seconds idle before the timed window")
-    p.add_argument("--cpu-rows", type=int, default=2048,
+    p.add_argument("--cpu-rows", type=int, default=8192,
                    help="rows of A in the oracle's timed slab (0 skips the CPU baseline)")
     args = p.parse_args(argv)
 

@@ -6,11 +6,15 @@ Every call goes through the C ABI via the ctypes binding.  The bar:
   integer, so any summation order gives the oracle's C16);
 * Gaussian inputs with unit-variance outputs: max |C_gpu - C64| <= 1e-2, the
   tolerance the pages use for fp32-accumulating kernels ("6. Four Consumers,
-  FP16 Accumulation, and a TMA Epilogue", "The Register Budget Problem"),
-  and, tighter, every output within one fp16 ulp of C16 = rne(C64) with at
-  least 99% of them bit-equal: fp32 accumulation moves the sum by ~1e-6, far
-  less than half an fp16 ulp, so only values sitting on a rounding boundary
-  may land on the neighbouring fp16 value.
+  FP16 Accumulation, and a TMA Epilogue", "The Register Budget Problem");
+  and, tighter, per element |C_gpu - C64| <= ulp16(C64) / 2 + e_acc, with at
+  least 99% of outputs bit-equal to C16 = rne(C64).  The fp16 cast alone
+  contributes at most half an fp16 ulp of the result.  e_acc bounds the fp32
+  accumulation: partial sums have magnitude ~1, each fp32 addition rounds by
+  at most 2^-24 of that, and the roundings add like a random walk over K
+  terms, giving ~2^-24 * sqrt(K); e_acc = 64 * 2^-24 * sqrt(K) leaves a wide
+  margin (3.4e-4 at K = 8192) yet still catches a truncating cast, which
+  errs by up to a whole ulp (3.9e-3 for |C| in [4, 8)).
 """
 from __future__ import annotations
 
@@ -60,14 +64,14 @@ def fp16_ulp(x):
     return np.exp2(np.floor(np.log2(ax)) - 10)
 
 
-def assert_close(got16, c64, c16, label=""):
+def assert_close(got16, c64, c16, K, label=""):
     got = got16.astype(np.float64)
     assert np.all(np.isfinite(got)), label + ": non-finite output"
     err = np.abs(got - c64)
     assert err.max() <= TOL, "%s: max err %g" % (label, err.max())
-    ref = c16.astype(np.float64)
-    step = fp16_ulp(np.maximum(np.abs(got), np.abs(ref)))
-    assert np.all(np.abs(got - ref) <= step), label + ": more than one fp16 ulp from rne(C64)"
+    bound = fp16_ulp(c64) / 2 + 64 * 2.0 ** -24 * np.sqrt(max(K, 1))
+    worst = np.max(err - bound)
+    assert worst <= 0, "%s: error exceeds half an fp16 ulp + fp32 bound by %g" % (label, worst)
     same = np.mean(got16.view(np.uint16) == c16.view(np.uint16))
     assert same >= 0.99, "%s: only %.4f bit-equal to rne(C64)" % (label, same)
     return err
@@ -102,7 +106,7 @@ def test_workload_full_parity(name):
     print("case", name, binding.gemm_nt_f16_config_name(w.M, w.N, w.K), flush=True)
     got = run(a, b)
     c64, c16 = workload_oracle(name)
-    err = assert_close(got, c64, c16, name)
+    err = assert_close(got, c64, c16, w.K, name)
     print("%s: max %.3g mean %.3g" % (name, err.max(), err.mean()))
 
 
@@ -125,7 +129,7 @@ def test_headline_sampled_parity_and_error_figures():
                            np.full(w.M, w.N - 1), g.integers(0, w.N, 65536)])
     c64 = oracle.gemm_nt_entries(a, b, rows, cols)
     c16 = oracle.encode_rne(c64).view(np.float16)
-    err = assert_close(got[rows, cols], c64, c16, name)
+    err = assert_close(got[rows, cols], c64, c16, w.K, name)
     assert abs(err.mean() - 1.4e-4) < 0.3e-4, err.mean()
     assert err.max() <= 2.0e-3 + 1e-5
     signed = (got[rows, cols].astype(np.float64) - c64).mean()
@@ -166,10 +170,17 @@ def test_identity_b_gives_a():
 
 
 def test_scaling_by_two_is_exact():
+    # doubling A doubles every product and every fp32 partial sum exactly;
+    # the fp16 cast commutes with doubling wherever the result is a normal
+    # fp16 value (the subnormal grid below 2^-14 is fixed, so there a
+    # doubled value can round differently)
     a, b = workloads.gaussian(384, 320, 512, seed=32)
-    c1 = run(a, b)
-    c2 = run((a.astype(np.float32) * 2).astype(np.float16), b)
-    assert np.array_equal(c2.astype(np.float64), 2.0 * c1.astype(np.float64))
+    c1 = run(a, b).astype(np.float64)
+    c2 = run((a.astype(np.float32) * 2).astype(np.float16), b).astype(np.float64)
+    normal = np.abs(c1) >= 2.0 ** -14
+    assert normal.mean() > 0.99
+    assert np.array_equal(c2[normal], 2.0 * c1[normal])
+    assert np.all(np.abs(c2[~normal] - 2.0 * c1[~normal]) <= 2.0 ** -23)
 
 
 def test_transpose_symmetry():
@@ -241,7 +252,7 @@ def test_k_not_multiple_of_8_uses_simple_path():
         a, b = workloads.gaussian(M, N, K, seed=K)
         print("case k%8", M, N, K, binding.gemm_nt_f16_config_name(M, N, K), flush=True)
         c64, c16 = oracle.gemm_nt(a, b)
-        assert_close(run(a, b), c64, c16, "K=%d" % K)
+        assert_close(run(a, b), c64, c16, K, "K=%d" % K)
 
 
 def test_unaligned_pointers_use_simple_path():
@@ -257,7 +268,7 @@ def test_unaligned_pointers_use_simple_path():
     ta, tb = ba[1:].view(M, K), bb[1:].view(N, K)
     c = binding.gemm_nt_f16(ta, tb)
     torch.cuda.synchronize()
-    assert_close(c.cpu().numpy(), c64, c16, "unaligned")
+    assert_close(c.cpu().numpy(), c64, c16, K, "unaligned")
     with pytest.raises(binding.GemmError):
         binding.gemm_nt_f16_ex(ta, tb, variant=0)
 
@@ -319,4 +330,4 @@ def test_non_default_stream():
     with torch.cuda.stream(s):
         c = binding.gemm_nt_f16(ta, tb)
     s.synchronize()
-    assert_close(c.cpu().numpy(), c64, c16, "side stream")
+    assert_close(c.cpu().numpy(), c64, c16, 264, "side stream")
