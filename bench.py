@@ -79,6 +79,9 @@ def main(argv=None) -> int:
     p.add_argument("--cooldown", type=float, default=3.0, help="seconds idle before the timed window")
     p.add_argument("--cpu-rows", type=int, default=8192,
                    help="rows of A in the oracle's timed slab (0 skips the CPU baseline)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="after timing, run one plain device copy of this many MiB (a kernel of "
+                        "known traffic, to scale hardware byte counters against)")
     args = p.parse_args(argv)
 
     if args.gpus != 1:
@@ -138,6 +141,17 @@ def main(argv=None) -> int:
     if not torch.isfinite(out.float()).all().item():
         print("bench.py: non-finite output", file=sys.stderr)
         return 1
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * 2 ** 20 // 2
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: copied %d MiB device to device (reads and writes %d bytes each)"
+            % (args.copy_calibration, 2 * n))
+        del src, dst
 
     roof = {
         "bound": "mfma",

@@ -45,6 +45,8 @@
 
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gemm_nt_f16.h"
 
 namespace {
@@ -52,6 +54,7 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -92,34 +95,97 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
     tn = r / rows;
 }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+// Compile-time tile configuration.
+//   BM x BN   output tile of one workgroup
+//   BK        K depth of one pipeline step (32 or 64 fp16 = 64 or 128 bytes
+//             per LDS row)
+//   WAVES_M x WAVES_N waves, each owning a (BM / WAVES_M) x (BN / WAVES_N)
+//             sub-tile of C, i.e. FM x FN blocks of 32 x 32
+//   STAGES    depth of the LDS ring: loads run STAGES - 1 steps ahead
+//   MIN_WAVES_PER_SIMD  occupancy hint (1: up to 512 registers per lane, the
+//             256 AGPRs holding the accumulator; 2: up to 256)
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_>
 struct TileShape {
-    static constexpr int BM = BM_, BN = BN_, BK = 64;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M * WAVES_N, THREADS = WAVES * kWave;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave sub-tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;            // 32x32 blocks per wave
+    static constexpr int KK = BK / 16;                             // MFMA k sub-steps per step
     static constexpr int STAGES = STAGES_;
-    static constexpr int ROW_BYTES = BK * 2;                       // 128
+    static constexpr int OCC = OCC_;
+    static constexpr int ROW_BYTES = BK * 2;
+    static constexpr int CHUNKS = ROW_BYTES / 16;                  // 16-byte chunks per row
+    // LDS serves 64 banks x 4 bytes = 256 bytes per cycle; a 16-byte read of
+    // 16 lanes covers it exactly.  Rows that share a 256-byte line
+    // (ROWS_PER_LINE of them) already sit on different banks, so the chunk
+    // position is XOR-ed with the row's line index: the 16 rows read by 16
+    // consecutive lanes at one logical chunk then hit 16 distinct bank groups.
+    static constexpr int ROWS_PER_LINE = 256 / ROW_BYTES;
+    static constexpr int SWZ_SHIFT = ROWS_PER_LINE == 2 ? 1 : 2;
+    static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;         // rows per 1 KiB wave load
     static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
-    // LDS: all A stages, then all B stages (keeps every offset inside the
-    // 16-bit immediate of ds_read for each operand's own base register)
-    static constexpr int B_BASE = STAGES * A_BYTES;
-    static constexpr int LDS_BYTES = STAGES * (A_BYTES + B_BYTES);
-    static constexpr int A_LOADS = A_BYTES / (kWave * 16) / WAVES;  // 1 KiB per wave load
-    static constexpr int B_LOADS = B_BYTES / (kWave * 16) / WAVES;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;         // 1 KiB per wave load
+    static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
+    static constexpr int LOADS = A_LOADS + B_LOADS;                // per wave per step
+    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static_assert(ROWS_PER_LINE * CHUNKS == 16, "swizzle covers 16 lanes");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(A_LOADS * WAVES * kWave * 16 == A_BYTES, "A tile must split evenly over waves");
-    static_assert(B_LOADS * WAVES * kWave * 16 == B_BYTES, "B tile must split evenly over waves");
+    static_assert(A_LOADS * WAVES * 1024 == A_BYTES, "A tile must split evenly over waves");
+    static_assert(B_LOADS * WAVES * 1024 == B_BYTES, "B tile must split evenly over waves");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
-    static_assert(A_BYTES <= 65536 && B_BYTES * STAGES <= 65536, "ds_read offsets");
+    static_assert(STAGES >= 2 && LOADS * (STAGES - 2) <= 63, "vmcnt holds at most 63");
 };
+
+template <class T>
+__device__ __forceinline__ int swz(int row, int chunk)
+{
+    return chunk ^ ((row >> T::SWZ_SHIFT) & (T::CHUNKS - 1));
+}
+
+// Epilogue: fp32 -> fp16 (round to nearest even) and store.  In each 32x32
+// block lane l holds row cm (= its row of the first block) and, in
+// accumulator registers 4q .. 4q+3, the four consecutive columns
+// cn + 8q .. cn + 8q + 3, written with one 8-byte store.  Rows past M and
+// columns past N are not written.
+template <class T>
+__device__ __forceinline__ void epilogue(const float16_t (&acc)[T::FM][T::FN], _Float16* __restrict__ C,
+                                         int M, int N, int cm, int cn, int c_vec)
+{
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+        const int m = cm + i * 32;
+        if (m >= M) continue;
+        _Float16* crow = C + (size_t)m * N;
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = cn + j * 32 + 8 * q;
+                half4_t h;
+                h[0] = (_Float16)acc[i][j][4 * q + 0];
+                h[1] = (_Float16)acc[i][j][4 * q + 1];
+                h[2] = (_Float16)acc[i][j][4 * q + 2];
+                h[3] = (_Float16)acc[i][j][4 * q + 3];
+                if (c_vec && n + 3 < N) {
+                    *(half4_t*)(crow + n) = h;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) crow[n + e] = h[e];
+                }
+            }
+        }
+    }
+}
 
 // Main MFMA kernel.  Requirements checked on the host: A and B 16-byte
 // aligned, K % 8 == 0, K < 2^22, M, N < 2^31.  `c_vec` says whether C rows
 // allow aligned 8-byte stores (N % 4 == 0 and C 8-byte aligned).
 template <class T>
-__global__ void __launch_bounds__(T::THREADS, 1)
+__global__ void __launch_bounds__(T::THREADS, T::OCC)
 gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                  _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
                  int group_m, int c_vec)
@@ -142,44 +208,63 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * row_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * row_bytes);
 
-    // Global->LDS copy assignment.  Load j of this wave fills LDS bytes
-    // [g * 1024, g * 1024 + 1024) of the operand tile, g = wave * LOADS + j:
-    // rows 8g .. 8g+7; lane l writes position (l & 7) of row 8g + l / 8, so it
-    // fetches logical chunk (l & 7) ^ (row & 7) = (l & 7) ^ (l / 8).
-    const int ld_row = lane >> 3;
-    const int ld_chunk = (lane & 7) ^ ld_row;
-    const uint32_t ld_voff = (uint32_t)ld_row * row_bytes + (uint32_t)ld_chunk * 16u;
-    const int ld_k = ld_chunk * 8;  // first k of this lane's chunk within the step
+    // Global->LDS copy assignment.  Load j of this wave fills bytes
+    // [g * 1024, g * 1024 + 1024) of the operand's tile in the stage,
+    // g = wave * LOADS + j, i.e. ROWS_PER_LOAD whole rows; lane l writes
+    // position l % CHUNKS of row g * ROWS_PER_LOAD + l / CHUNKS, so it
+    // fetches the logical chunk that the swizzle puts at that position.
+    const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
+    uint32_t a_voff[T::A_LOADS], b_voff[T::B_LOADS];
+    int a_kc[T::A_LOADS], b_kc[T::B_LOADS];  // first k of the fetched chunk
+#pragma unroll
+    for (int j = 0; j < T::A_LOADS; ++j) {
+        const int row = (wave * T::A_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
+        const int c = swz<T>(row, ld_p);
+        a_voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
+        a_kc[j] = c * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < T::B_LOADS; ++j) {
+        const int row = (wave * T::B_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
+        const int c = swz<T>(row, ld_p);
+        b_voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
+        b_kc[j] = c * 8;
+    }
 
+    // Issues the loads of step `kstep` into `stage`.  Steps past the end of
+    // K load zeros (every chunk is out of range), so the ring can run without
+    // branches; those stages are never read.
     auto issue_loads = [&](int stage, int kstep) {
         const int k0 = kstep * T::BK;
-        // K tail: chunks at or past K read as zero (both operands), so the
-        // padded products add nothing.
-        const uint32_t voff = (k0 + ld_k < K) ? ld_voff : kOob;
+        const int krem = K - k0;  // chunks starting at or past K read as zero
         const uint32_t soff = (uint32_t)k0 * 2u;
+        unsigned char* a_dst = smem + stage * T::STAGE_BYTES + wave * T::A_LOADS * 1024;
+        unsigned char* b_dst = smem + stage * T::STAGE_BYTES + T::A_BYTES + wave * T::B_LOADS * 1024;
 #pragma unroll
         for (int j = 0; j < T::A_LOADS; ++j) {
-            const int g = wave * T::A_LOADS + j;
-            const uint32_t v = voff == kOob ? kOob : voff + (uint32_t)(g * 8) * row_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void_t*)(smem + stage * T::A_BYTES + g * 1024), 16, v, soff, 0, 0);
+            const uint32_t v = a_kc[j] < krem ? a_voff[j] : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(a_dst + j * 1024), 16, v, soff,
+                                                     0, 0);
         }
 #pragma unroll
         for (int j = 0; j < T::B_LOADS; ++j) {
-            const int g = wave * T::B_LOADS + j;
-            const uint32_t v = voff == kOob ? kOob : voff + (uint32_t)(g * 8) * row_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void_t*)(smem + T::B_BASE + stage * T::B_BYTES + g * 1024), 16, v, soff,
-                0, 0);
+            const uint32_t v = b_kc[j] < krem ? b_voff[j] : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(b_dst + j * 1024), 16, v, soff,
+                                                     0, 0);
         }
     };
 
     // Fragment reads: row (l % 32) of each 32-row block, logical chunk
-    // 2 * kk + l / 32 for k sub-step kk (16 k values per MFMA).
+    // 2 * kk + l / 32 for k sub-step kk (16 k values per MFMA).  Row offsets
+    // within a block are multiples of 32, so the swizzle term depends only on
+    // l % 32 and is the same for every block.
     const int fr_row = lane & 31;
     const int fr_hi = lane >> 5;
-    const unsigned char* a_lds = smem + (wm * T::WTM + fr_row) * T::ROW_BYTES;
-    const unsigned char* b_lds = smem + T::B_BASE + (wn * T::WTN + fr_row) * T::ROW_BYTES;
+    const int a_row0 = wm * T::WTM + fr_row;
+    const int b_row0 = wn * T::WTN + fr_row;
+    int fr_pos[T::KK];
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, 2 * kk + fr_hi) * 16;
 
     half8_t fa[2][T::FM], fb[2][T::FN];
     float16_t acc[T::FM][T::FN];
@@ -190,14 +275,13 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto read_frags = [&](int buf, int stage, int kk) {
-        const int pos = ((2 * kk + fr_hi) ^ (fr_row & 7)) * 16;
+    auto read_frags = [&](int buf, const unsigned char* stage_base, int kk) {
+        const unsigned char* pa = stage_base + a_row0 * T::ROW_BYTES + fr_pos[kk];
+        const unsigned char* pb = stage_base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[kk];
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-            fa[buf][i] = *(const half8_t*)(a_lds + stage * T::A_BYTES + i * 32 * T::ROW_BYTES + pos);
+        for (int i = 0; i < T::FM; ++i) fa[buf][i] = *(const half8_t*)(pa + i * 32 * T::ROW_BYTES);
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j)
-            fb[buf][j] = *(const half8_t*)(b_lds + stage * T::B_BYTES + j * 32 * T::ROW_BYTES + pos);
+        for (int j = 0; j < T::FN; ++j) fb[buf][j] = *(const half8_t*)(pb + j * 32 * T::ROW_BYTES);
     };
 
     auto mma = [&](int buf) {
@@ -211,74 +295,432 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 
     const int nk = (K + T::BK - 1) / T::BK;
 
-    // Two-stage ring.  Invariant at the top of step ks: stage ks & 1 holds
-    // step ks and is visible to all waves; the loads of step ks + 1 are in
-    // flight into the other stage; fa/fb[0] hold sub-step 0 of step ks.
-    // Sub-step 3's MFMAs run after the barrier, overlapping the first
-    // fragment reads of the next stage.
-    static_assert(T::STAGES == 2, "ring below is written for two stages");
+    // STAGES-deep ring.  Step ks lives in stage ks % STAGES; its loads are
+    // issued STAGES - 1 steps earlier.  Before step ks + 1 is read, each wave
+    // waits until its own loads of that step have landed (vmcnt: only the
+    // loads of the STAGES - 2 later steps may still be outstanding) and a
+    // barrier makes all waves' loads visible; the same barrier (its fence
+    // drains this wave's LDS reads) also guarantees every wave has finished
+    // reading step ks's stage, which is then refilled with step ks + STAGES.
+    //
+    // Issue order inside a step (pinned with scheduling-group barriers, so
+    // the matrix core always has independent work queued):
+    //   sub-steps 0 .. KK-2:  fragment reads of sub-step kk+1, then the
+    //                         FM*FN MFMAs of sub-step kk;
+    //   after the barrier:    fragment reads of the next step's sub-step 0,
+    //                         then the MFMAs of sub-step KK-1, each followed
+    //                         by one of the wave's global->LDS loads.
     if (nk > 0) {
-        issue_loads(0, 0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+#pragma unroll
+        for (int s = 0; s < T::STAGES - 1; ++s) issue_loads(s, s);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::LOADS * (T::STAGES - 2)));
         __syncthreads();
-        if (nk > 1) issue_loads(1, 1);
-        read_frags(0, 0, 0);
+        issue_loads(T::STAGES - 1, T::STAGES - 1);
+        read_frags(0, smem, 0);
 
-        auto step = [&](int ks, int cur) {
-            read_frags(1, cur, 1);
-            mma(0);
-            read_frags(0, cur, 2);
-            mma(1);
-            read_frags(1, cur, 3);
-            mma(0);
-            if (ks + 1 < nk) {
-                // own loads of step ks+1 landed; the barrier makes everyone's
-                // visible and (its fence drains LDS reads) frees stage `cur`
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-                __syncthreads();
-                if (ks + 2 < nk) issue_loads(cur, ks + 2);
-                read_frags(0, cur ^ 1, 0);
+        int cur = 0;  // stage of step ks
+        for (int ks = 0; ks < nk; ++ks) {
+            const unsigned char* base = smem + cur * T::STAGE_BYTES;
+            const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
+#pragma unroll
+            for (int kk = 0; kk + 1 < T::KK; ++kk) {
+                read_frags((kk + 1) & 1, base, kk + 1);
+                mma(kk & 1);
             }
-            mma(1);
-        };
-
-        int ks = 0;
-        for (; ks + 1 < nk; ks += 2) {
-            step(ks, 0);
-            step(ks + 1, 1);
+#pragma unroll
+            for (int kk = 0; kk + 1 < T::KK; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, T::FM * T::FN, 0);  // MFMAs
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::LOADS * (T::STAGES - 2)));
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(T::KK & 1, smem + nxt * T::STAGE_BYTES, 0);
+            issue_loads(cur, ks + T::STAGES);
+            mma((T::KK - 1) & 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
+#pragma unroll
+            for (int i = 0; i < T::FM * T::FN; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);          // one MFMA
+                if (i < T::LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // one load
+            }
+            cur = nxt;
         }
-        if (ks < nk) step(ks, 0);
+        // no global->LDS load may still be writing when the workgroup ends
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
 
-    // Epilogue: fp32 -> fp16 (round to nearest even), 4 consecutive columns
-    // per 8-byte store; rows past M and columns past N are not written.
-    const int cm_base = m0 + wm * T::WTM + fr_row;
-    const int cn_base = n0 + wn * T::WTN + 4 * fr_hi;
+    epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
+}
+
+// Persistent streaming variant of the kernel above.  The grid holds one
+// workgroup per compute unit; workgroup b computes tiles b, b + G, b + 2G, ...
+// (G = grid size) in the raster order of tile_coords.  The load cursor runs
+// through that tile sequence as one continuous stream of K steps: while the
+// last steps of a tile are computed, the first steps of the next tile are
+// already being loaded, so a tile change costs only the epilogue (no pipeline
+// drain and refill, no workgroup relaunch).  Past the last tile the cursor
+// reads from empty buffers, which return zeros into stages never read again.
+template <class T>
+__global__ void __launch_bounds__(T::THREADS, T::OCC)
+gemm_nt_f16_stream(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
+                   _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+                   int group_m, int c_vec)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+    const int total = tiles_m * tiles_n;
+    const int nk = (K + T::BK - 1) / T::BK;
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+
+    const int fr_row = lane & 31;
+    const int fr_hi = lane >> 5;
+
+    float16_t acc[T::FM][T::FN];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-        const int m = cm_base + i * 32;
-        if (m >= M) continue;
-        _Float16* crow = C + (size_t)m * N;
+        for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
+            for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = cn_base + j * 32 + 8 * q;
-                half4_t h;
-                h[0] = (_Float16)acc[i][j][4 * q + 0];
-                h[1] = (_Float16)acc[i][j][4 * q + 1];
-                h[2] = (_Float16)acc[i][j][4 * q + 2];
-                h[3] = (_Float16)acc[i][j][4 * q + 3];
-                if (c_vec && n + 3 < N) {
-                    *(half4_t*)(crow + n) = h;
-                } else {
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    };
+
+    if (nk == 0) {  // empty sum: every output is +0
+        zero_acc();
+        for (int t = blockIdx.x; t < total; t += gridDim.x) {
+            int tm, tn;
+            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+            epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
+                        tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
+        }
+        return;
+    }
+
+    // Global->LDS copy assignment (independent of the tile): load j of this
+    // wave fills bytes [g * 1024, g * 1024 + 1024) of the operand's tile in
+    // the stage, g = wave * LOADS + j, i.e. ROWS_PER_LOAD whole rows; lane l
+    // writes position l % CHUNKS of row g * ROWS_PER_LOAD + l / CHUNKS, so it
+    // fetches the logical chunk that the swizzle puts at that position.
+    const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
+    uint32_t a_voff[T::A_LOADS], b_voff[T::B_LOADS];
+    int a_kc[T::A_LOADS], b_kc[T::B_LOADS];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) crow[n + e] = h[e];
+    for (int j = 0; j < T::A_LOADS; ++j) {
+        const int row = (wave * T::A_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
+        const int c = swz<T>(row, ld_p);
+        a_voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
+        a_kc[j] = c * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < T::B_LOADS; ++j) {
+        const int row = (wave * T::B_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
+        const int c = swz<T>(row, ld_p);
+        b_voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
+        b_kc[j] = c * 8;
+    }
+
+    // Load cursor: tile ld_tile, step ld_ks; ld_ra / ld_rb cover that tile's
+    // rows (rows past M or N read as zero; past the last tile, everything).
+    int ld_tile = blockIdx.x, ld_ks = 0;
+    __amdgpu_buffer_rsrc_t ld_ra, ld_rb;
+    auto set_load_tile = [&](int t) {
+        if (t < total) {
+            int tm, tn;
+            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+            const int m0 = tm * T::BM, n0 = tn * T::BN;
+            ld_ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(T::BM, M - m0) * row_bytes);
+            ld_rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)min(T::BN, N - n0) * row_bytes);
+        } else {
+            ld_ra = make_rsrc(A, 0u);
+            ld_rb = make_rsrc(B, 0u);
+        }
+    };
+    auto advance_cursor = [&]() {
+        if (++ld_ks == nk) {
+            ld_ks = 0;
+            ld_tile += gridDim.x;
+            set_load_tile(ld_tile);
+        }
+    };
+    // Loads of the cursor's step into `stage`.  K tail: chunks at or past K
+    // read as zero for both operands, so the padding adds nothing.
+    auto issue_loads = [&](int stage) {
+        const int k0 = ld_ks * T::BK;
+        const int krem = K - k0;
+        const uint32_t soff = (uint32_t)k0 * 2u;
+        unsigned char* a_dst = smem + stage * T::STAGE_BYTES + wave * T::A_LOADS * 1024;
+        unsigned char* b_dst = smem + stage * T::STAGE_BYTES + T::A_BYTES + wave * T::B_LOADS * 1024;
+#pragma unroll
+        for (int j = 0; j < T::A_LOADS; ++j) {
+            const uint32_t v = a_kc[j] < krem ? a_voff[j] : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_ra, (lds_void_t*)(a_dst + j * 1024), 16, v, soff,
+                                                     0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < T::B_LOADS; ++j) {
+            const uint32_t v = b_kc[j] < krem ? b_voff[j] : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_rb, (lds_void_t*)(b_dst + j * 1024), 16, v, soff,
+                                                     0, 0);
+        }
+    };
+
+    const int a_row0 = wm * T::WTM + fr_row;
+    const int b_row0 = wn * T::WTN + fr_row;
+    int fr_pos[T::KK];
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, 2 * kk + fr_hi) * 16;
+
+    half8_t fa[2][T::FM], fb[2][T::FN];
+    auto read_frags = [&](int buf, const unsigned char* stage_base, int kk) {
+        const unsigned char* pa = stage_base + a_row0 * T::ROW_BYTES + fr_pos[kk];
+        const unsigned char* pb = stage_base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[kk];
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) fa[buf][i] = *(const half8_t*)(pa + i * 32 * T::ROW_BYTES);
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) fb[buf][j] = *(const half8_t*)(pb + j * 32 * T::ROW_BYTES);
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[buf][j], fa[buf][i], acc[i][j],
+                                                                   0, 0, 0);
+    };
+
+    // Prologue: steps 0 .. STAGES-2 of the first tile, wait for step 0.
+    set_load_tile(ld_tile);
+#pragma unroll
+    for (int s = 0; s < T::STAGES - 1; ++s) {
+        issue_loads(s);
+        advance_cursor();
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::LOADS * (T::STAGES - 2)));
+    __syncthreads();
+    issue_loads(T::STAGES - 1);
+    advance_cursor();
+    read_frags(0, smem, 0);
+
+    int cur = 0;  // stage of the step being computed
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        zero_acc();
+        for (int ks = 0; ks < nk; ++ks) {
+            const unsigned char* base = smem + cur * T::STAGE_BYTES;
+            const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
+#pragma unroll
+            for (int kk = 0; kk + 1 < T::KK; ++kk) {
+                read_frags((kk + 1) & 1, base, kk + 1);
+                mma(kk & 1);
+            }
+#pragma unroll
+            for (int kk = 0; kk + 1 < T::KK; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, T::FM * T::FN, 0);  // MFMAs
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // Loads of the next step have landed (only the STAGES - 2 steps
+            // after it may be outstanding; after an epilogue its stores are
+            // outstanding too, so wait for everything there).
+            if (T::STAGES == 2 || ks == 0)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::LOADS * (T::STAGES - 2)));
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(T::KK & 1, smem + nxt * T::STAGE_BYTES, 0);
+            issue_loads(cur);
+            mma((T::KK - 1) & 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
+#pragma unroll
+            for (int i = 0; i < T::FM * T::FN; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);          // one MFMA
+                if (i < T::LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // one load
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            advance_cursor();
+            cur = nxt;
+        }
+        int tm, tn;
+        tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+        epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
+                    tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
+    }
+    // no global->LDS load may still be writing when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+// MFMA kernel with register-staged global loads.  Global data travels
+// global -> VGPRs -> LDS through two register sets and two LDS stages: the
+// tile of step s is loaded into a register set during step s - 3, written to
+// LDS stage s % 2 during step s - 1 and read during step s.  Loads therefore
+// have two steps of matrix-core time to arrive (a direct-to-LDS load into a
+// two-stage ring has one), and the per-step barrier never waits on global
+// memory, only on this step's LDS traffic.
+//
+// Step ks (LDS stage p = ks & 1):
+//   region 1  MFMA sub-steps 0 .. KK-2 of step ks, fragment reads one
+//             sub-step ahead; interleaved with them, the LDS writes of step
+//             ks+1 (register set p^1 -> stage p^1) each followed by the
+//             global load of step ks+3 into the register it just freed;
+//   barrier   (this wave's LDS reads and writes complete): every wave is done
+//             reading stage p, and step ks+1 is visible in stage p^1;
+//   region 2  fragment reads of step ks+1 sub-step 0, then the MFMAs of
+//             sub-step KK-1 of step ks.
+// Steps past the end of K load zeros, so the loop runs an even number of
+// steps (a zero step adds nothing) and needs no tail code.
+template <class T>
+__global__ void __launch_bounds__(T::THREADS, T::OCC)
+gemm_nt_f16_mfma_vgpr(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
+                      _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+                      int group_m, int c_vec)
+{
+    static_assert(T::STAGES == 2, "two LDS stages, two register sets");
+    constexpr int WPS = (T::LOADS + T::KK - 2) / (T::KK - 1);  // LDS writes per sub-step
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * row_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * row_bytes);
+
+    // Load j of this wave covers tile bytes [g * 1024, g * 1024 + 1024),
+    // g = wave * A_LOADS + j for A (j < A_LOADS), likewise for B:
+    // ROWS_PER_LOAD whole rows, lane l reading logical chunk l % CHUNKS of
+    // row g * ROWS_PER_LOAD + l / CHUNKS (coalesced) and writing it at its
+    // swizzled LDS position.  A row offset stays below 2^31 (K < 2^22, rows
+    // < 256), so adding 2^31 pushes a load past any buffer: it reads zero.
+    const int ld_r = lane / T::CHUNKS, ld_c = lane % T::CHUNKS;
+    const int ld_kc = ld_c * 8;
+    uint32_t voff[T::LOADS];
+    int lds_off[T::LOADS];
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) {
+        const bool is_a = j < T::A_LOADS;
+        const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
+        const int row = g * T::ROWS_PER_LOAD + ld_r;
+        voff[j] = (uint32_t)row * row_bytes + (uint32_t)ld_c * 16u;
+        lds_off[j] = (is_a ? 0 : T::A_BYTES) + row * T::ROW_BYTES + swz<T>(row, ld_c) * 16;
+    }
+
+    u32x4_t regs[2][T::LOADS];
+    auto gload_one = [&](u32x4_t (&dst)[T::LOADS], int j, int kstep) {
+        const int k0 = kstep * T::BK;
+        const uint32_t oob = ld_kc < K - k0 ? 0u : kOob;  // K tail and steps past K read zero
+        dst[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 j < T::A_LOADS ? ra : rb, (int)(voff[j] + oob), k0 * 2, 0));
+    };
+    auto lstore_one = [&](const u32x4_t (&src)[T::LOADS], int j, int stage) {
+        *(u32x4_t*)(smem + stage * T::STAGE_BYTES + lds_off[j]) = src[j];
+    };
+
+    const int fr_row = lane & 31;
+    const int fr_hi = lane >> 5;
+    const int a_row0 = wm * T::WTM + fr_row;
+    const int b_row0 = wn * T::WTN + fr_row;
+    int fr_pos[T::KK];
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, 2 * kk + fr_hi) * 16;
+
+    half8_t fa[2][T::FM], fb[2][T::FN];
+    float16_t acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto read_frags = [&](int buf, int stage, int kk) {
+        const unsigned char* base = smem + stage * T::STAGE_BYTES;
+        const unsigned char* pa = base + a_row0 * T::ROW_BYTES + fr_pos[kk];
+        const unsigned char* pb = base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[kk];
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) fa[buf][i] = *(const half8_t*)(pa + i * 32 * T::ROW_BYTES);
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) fb[buf][j] = *(const half8_t*)(pb + j * 32 * T::ROW_BYTES);
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[buf][j], fa[buf][i], acc[i][j],
+                                                                   0, 0, 0);
+    };
+    // Workgroup barrier that orders LDS traffic only: this wave's LDS reads
+    // and writes are complete, global loads may stay in flight.
+    auto lds_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    const int nk = (K + T::BK - 1) / T::BK;
+    const int nk2 = (nk + 1) & ~1;
+
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) gload_one(regs[0], j, 0);
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) gload_one(regs[1], j, 1);
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) lstore_one(regs[0], j, 0);
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) gload_one(regs[0], j, 2);
+    lds_barrier();
+    read_frags(0, 0, 0);
+
+    auto step = [&](int ks, int p) {
+#pragma unroll
+        for (int kk = 0; kk + 1 < T::KK; ++kk) {
+            read_frags((kk + 1) & 1, p, kk + 1);
+            mma(kk & 1);
+#pragma unroll
+            for (int w = 0; w < WPS; ++w) {
+                const int j = kk * WPS + w;
+                if (j < T::LOADS) {
+                    lstore_one(regs[p ^ 1], j, p ^ 1);
+                    gload_one(regs[p ^ 1], j, ks + 3);
                 }
             }
         }
+#pragma unroll
+        for (int kk = 0; kk + 1 < T::KK; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
+#pragma unroll
+            for (int i = 0; i < T::FM * T::FN; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+                if (i < WPS && kk * WPS + i < T::LOADS) {
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // one LDS write
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // one global load
+                }
+            }
+        }
+        lds_barrier();
+        read_frags(T::KK & 1, p ^ 1, 0);
+        mma((T::KK - 1) & 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);      // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, T::FM * T::FN, 1);      // MFMAs
+    };
+    for (int ks = 0; ks < nk2; ks += 2) {
+        step(ks, 0);
+        step(ks + 1, 1);
     }
+
+    epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
 }
 
 // Plain per-element kernel for inputs the MFMA kernels do not take
@@ -300,9 +742,14 @@ gemm_nt_f16_simple(const _Float16* __restrict__ A, const _Float16* __restrict__ 
 
 // ------------------------------------------------------------------ host --
 
-typedef TileShape<256, 256, 2, 2, 2> Tile256;
-typedef TileShape<128, 128, 2, 2, 2> Tile128;
-typedef TileShape<64, 64, 2, 2, 2> Tile64;
+//                  BM   BN   BK  WM  WN  S  OCC
+typedef TileShape<256, 256, 64, 2, 2, 2, 1> T256_k64_s2_w4;
+typedef TileShape<256, 256, 32, 2, 2, 4, 1> T256_k32_s4_w4;
+typedef TileShape<256, 256, 32, 2, 4, 4, 2> T256_k32_s4_w8;
+typedef TileShape<256, 256, 64, 2, 4, 2, 2> T256_k64_s2_w8;
+typedef TileShape<256, 128, 64, 2, 2, 3, 1> T256x128_k64_s3_w4;
+typedef TileShape<128, 128, 64, 2, 2, 3, 1> T128_k64_s3_w4;
+typedef TileShape<64, 64, 64, 2, 2, 3, 2> T64_k64_s3_w4;
 
 constexpr int64_t kMaxK = (int64_t)1 << 22;
 constexpr int64_t kMaxMN = ((int64_t)1 << 31) - 1;
@@ -327,6 +774,50 @@ int launch_mfma(const void* A, const void* B, void* C, int64_t M, int64_t N, int
     return (int)hipGetLastError();
 }
 
+template <class T>
+int launch_mfma_vgpr(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                     int group_m, hipStream_t stream)
+{
+    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
+    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
+    const int c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
+    hipLaunchKernelGGL((gemm_nt_f16_mfma_vgpr<T>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(T::THREADS), 0, stream, (const _Float16*)A, (const _Float16*)B,
+                       (_Float16*)C, (int)M, (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m,
+                       c_vec);
+    return (int)hipGetLastError();
+}
+
+int num_cus(int device)
+{
+    static int cache[64];
+    if (device < 0 || device >= 64) return 256;
+    int n = __atomic_load_n(&cache[device], __ATOMIC_RELAXED);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        __atomic_store_n(&cache[device], n, __ATOMIC_RELAXED);
+    }
+    return n;
+}
+
+template <class T>
+int launch_stream(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                  int group_m, hipStream_t stream)
+{
+    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
+    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) device = 0;
+    const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus(device));
+    const int c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
+    hipLaunchKernelGGL((gemm_nt_f16_stream<T>), dim3((unsigned)grid), dim3(T::THREADS), 0, stream,
+                       (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N,
+                       (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
+    return (int)hipGetLastError();
+}
+
 int launch_simple(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int,
                   hipStream_t stream)
 {
@@ -338,9 +829,17 @@ int launch_simple(const void* A, const void* B, void* C, int64_t M, int64_t N, i
 }
 
 const Variant kVariants[] = {
-    {"mfma32_256x256x64_w2x2_s2_g8", 256, 256, 8, launch_mfma<Tile256>},
-    {"mfma32_128x128x64_w2x2_s2_g8", 128, 128, 8, launch_mfma<Tile128>},
-    {"mfma32_64x64x64_w2x2_s2_g8", 64, 64, 8, launch_mfma<Tile64>},
+    {"mfma32_256x256x32_w4_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w4>},
+    {"mfma32_256x256x32_w8_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w8>},
+    {"mfma32_256x256x64_w4_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w4>},
+    {"mfma32_256x256x64_w8_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8>},
+    {"mfma32_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4>},
+    {"mfma32_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4>},
+    {"mfma32_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4>},
+    {"mfma32_256x256x64_w4_vgpr2", 256, 256, 8, launch_mfma_vgpr<T256_k64_s2_w4>},
+    {"mfma32_256x256x64_w8_vgpr2", 256, 256, 8, launch_mfma_vgpr<T256_k64_s2_w8>},
+    {"mfma32_256x256x64_w4_stream", 256, 256, 8, launch_stream<T256_k64_s2_w4>},
+    {"mfma32_256x256x64_w8_stream", 256, 256, 8, launch_stream<T256_k64_s2_w8>},
     {"simple_f32_per_element", 0, 0, 0, launch_simple},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -381,8 +880,8 @@ int select_mfma(int64_t M, int64_t N)
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (t256 >= 192) return 0;
-    if (t128 >= 128) return 1;
-    return 2;
+    if (t128 >= 128) return 5;
+    return 6;
 }
 
 }  // namespace

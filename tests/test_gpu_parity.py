@@ -247,6 +247,31 @@ def test_edge_shapes_every_variant():
             assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), (M, N, K, name)
 
 
+@pytest.mark.parametrize("M,N,K", [(5000, 6000, 72), (8192, 8192, 128), (2304, 9000, 8)])
+def test_many_tiles_per_workgroup_every_variant(M, N, K):
+    """Shapes with more tiles than compute units, so the persistent kernels
+    stream several tiles (and their K tails) through one workgroup."""
+    a, b = workloads.small_integers(M, N, K, seed=M + N + K)
+    _, c16 = oracle.gemm_nt(a, b)
+    for name, vid in variant_ids().items():
+        if name.startswith("simple") and M * N * K > 2 ** 32:
+            continue
+        print("case many-tiles", M, N, K, name, flush=True)
+        got = run(a, b, variant=vid)
+        assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), (M, N, K, name)
+
+
+def test_k_zero_many_tiles_every_variant():
+    torch = _torch()
+    a = torch.zeros((4096, 0), dtype=torch.float16, device=dev())
+    b = torch.zeros((4352, 0), dtype=torch.float16, device=dev())
+    for name, vid in variant_ids().items():
+        out = torch.full((4096, 4352), 5.0, dtype=torch.float16, device=dev())
+        binding.gemm_nt_f16_ex(a, b, out=out, variant=vid)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0).item(), name
+
+
 def test_k_not_multiple_of_8_uses_simple_path():
     for (M, N, K) in [(33, 17, 7), (64, 64, 1), (100, 90, 13), (5, 300, 999)]:
         a, b = workloads.gaussian(M, N, K, seed=K)
