@@ -555,6 +555,250 @@ gemm_nt_f16_stream(const _Float16* __restrict__ A, const _Float16* __restrict__ 
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
+// ---------------------------------------------------------------------------
+// Hand-scheduled main loop for the 256 x 256 tile with 4 waves (each wave a
+// 128 x 128 sub-tile = 4 x 4 blocks of 32 x 32, 256 fp32 accumulators per
+// lane in AGPRs) and BK = 64 (four k sub-steps of 16).  The issue order of a
+// sub-step is fixed in inline assembly so the compiler cannot regroup it:
+// the 16 MFMAs of sub-step kk run back to back while the 8 fragment reads of
+// sub-step kk+1 are interleaved between the first 8 of them.  Operand
+// registers are still chosen by the compiler.  Fragment reads issued inside
+// these blocks are invisible to the compiler's wait-count tracking, so each
+// block that consumes them starts with its own s_waitcnt lgkmcnt(0).
+// ---------------------------------------------------------------------------
+#define GEMM_MF(c, b, a) "v_mfma_f32_32x32x16_f16 %[" c "], %[" b "], %[" a "], %[" c "]\n\t"
+#define GEMM_DR(d, p, off) "ds_read_b128 %[" d "], %[" p "] offset:" #off "\n\t"
+#define GEMM_ACC_OPS(acc)                                                                    \
+    [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c02] "+a"(acc[0][2]), [c03] "+a"(acc[0][3]), \
+    [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]), [c12] "+a"(acc[1][2]), [c13] "+a"(acc[1][3]), \
+    [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c22] "+a"(acc[2][2]), [c23] "+a"(acc[2][3]), \
+    [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]), [c32] "+a"(acc[3][2]), [c33] "+a"(acc[3][3])
+
+// acc[i][j] += B-fragment j * A-fragment i for all 16 blocks; reads the next
+// sub-step's fragments (A rows at pa + 4096 i, B rows at pb + 4096 j).
+// The block first waits for the fragment reads issued before it.
+__device__ __forceinline__ void substep_4x4(float16_t (&acc)[4][4], const half8_t (&ca)[4],
+                                            const half8_t (&cb)[4], half8_t (&na)[4],
+                                            half8_t (&nb)[4], uint32_t pa, uint32_t pb)
+{
+    asm volatile(
+        "s_waitcnt lgkmcnt(0)\n\t"
+        GEMM_MF("c00", "b0", "a0") GEMM_DR("na0", "pa", 0)
+        GEMM_MF("c01", "b1", "a0") GEMM_DR("na1", "pa", 4096)
+        GEMM_MF("c02", "b2", "a0") GEMM_DR("na2", "pa", 8192)
+        GEMM_MF("c03", "b3", "a0") GEMM_DR("na3", "pa", 12288)
+        GEMM_MF("c10", "b0", "a1") GEMM_DR("nb0", "pb", 0)
+        GEMM_MF("c11", "b1", "a1") GEMM_DR("nb1", "pb", 4096)
+        GEMM_MF("c12", "b2", "a1") GEMM_DR("nb2", "pb", 8192)
+        GEMM_MF("c13", "b3", "a1") GEMM_DR("nb3", "pb", 12288)
+        GEMM_MF("c20", "b0", "a2") GEMM_MF("c21", "b1", "a2")
+        GEMM_MF("c22", "b2", "a2") GEMM_MF("c23", "b3", "a2")
+        GEMM_MF("c30", "b0", "a3") GEMM_MF("c31", "b1", "a3")
+        GEMM_MF("c32", "b2", "a3") GEMM_MF("c33", "b3", "a3")
+        : GEMM_ACC_OPS(acc),
+          [na0] "=&v"(na[0]), [na1] "=&v"(na[1]), [na2] "=&v"(na[2]), [na3] "=&v"(na[3]),
+          [nb0] "=&v"(nb[0]), [nb1] "=&v"(nb[1]), [nb2] "=&v"(nb[2]), [nb3] "=&v"(nb[3])
+        : [a0] "v"(ca[0]), [a1] "v"(ca[1]), [a2] "v"(ca[2]), [a3] "v"(ca[3]),
+          [b0] "v"(cb[0]), [b1] "v"(cb[1]), [b2] "v"(cb[2]), [b3] "v"(cb[3]),
+          [pa] "v"(pa), [pb] "v"(pb)
+        : "memory");
+}
+
+// The four MFMAs of block row i (acc[i][0..3]), no fragment reads.
+template <int I>
+__device__ __forceinline__ void mfma_row_4(float16_t (&acc)[4][4], const half8_t& ca,
+                                           const half8_t (&cb)[4])
+{
+    asm volatile(
+        "v_mfma_f32_32x32x16_f16 %[c0], %[b0], %[a], %[c0]\n\t"
+        "v_mfma_f32_32x32x16_f16 %[c1], %[b1], %[a], %[c1]\n\t"
+        "v_mfma_f32_32x32x16_f16 %[c2], %[b2], %[a], %[c2]\n\t"
+        "v_mfma_f32_32x32x16_f16 %[c3], %[b3], %[a], %[c3]\n\t"
+        : [c0] "+a"(acc[I][0]), [c1] "+a"(acc[I][1]), [c2] "+a"(acc[I][2]), [c3] "+a"(acc[I][3])
+        : [a] "v"(ca), [b0] "v"(cb[0]), [b1] "v"(cb[1]), [b2] "v"(cb[2]), [b3] "v"(cb[3])
+        : "memory");
+}
+
+// Eight fragment reads (A rows at pa + 4096 i, B rows at pb + 4096 j).
+__device__ __forceinline__ void read_frags_4x4(half8_t (&na)[4], half8_t (&nb)[4], uint32_t pa,
+                                               uint32_t pb)
+{
+    asm volatile(
+        GEMM_DR("na0", "pa", 0) GEMM_DR("na1", "pa", 4096) GEMM_DR("na2", "pa", 8192)
+        GEMM_DR("na3", "pa", 12288) GEMM_DR("nb0", "pb", 0) GEMM_DR("nb1", "pb", 4096)
+        GEMM_DR("nb2", "pb", 8192) GEMM_DR("nb3", "pb", 12288)
+        : [na0] "=&v"(na[0]), [na1] "=&v"(na[1]), [na2] "=&v"(na[2]), [na3] "=&v"(na[3]),
+          [nb0] "=&v"(nb[0]), [nb1] "=&v"(nb[1]), [nb2] "=&v"(nb[2]), [nb3] "=&v"(nb[3])
+        : [pa] "v"(pa), [pb] "v"(pb)
+        : "memory");
+}
+
+// Persistent streaming kernel with the hand-scheduled 4 x 4 main loop
+// (the same tile order, load cursor, LDS layout, K-tail handling and
+// epilogue as gemm_nt_f16_stream).  Per K step (stage p):
+//   three blocks: MFMAs of sub-steps 0, 1, 2, each with the next
+//     sub-step's fragment reads interleaved;
+//   s_waitcnt vmcnt(0) lgkmcnt(0); s_barrier: the next step's stage is
+//     loaded and visible, and every wave is done reading stage p;
+//   the MFMAs of sub-step 3 in four rows of four, the first row with the
+//     next step's sub-step-0 reads interleaved, each row followed by four
+//     global->LDS loads of step + 2 into stage p.
+template <class T>
+__global__ void __launch_bounds__(T::THREADS, T::OCC)
+gemm_nt_f16_asm(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
+                _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+                int group_m, int c_vec)
+{
+    static_assert(T::FM == 4 && T::FN == 4 && T::KK == 4 && T::STAGES == 2 && T::LOADS == 16,
+                  "the hand-scheduled loop is written for 4 x 4 blocks, BK = 64, 2 stages");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+    const int total = tiles_m * tiles_n;
+    const int nk = (K + T::BK - 1) / T::BK;
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+
+    const int fr_row = lane & 31;
+    const int fr_hi = lane >> 5;
+
+    float16_t acc[4][4];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        // accumulator writes must settle before an MFMA reads them
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+    };
+    auto finish_mfma = [&]() {
+        // the last MFMAs' results must be written before they are read
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    };
+
+    if (nk == 0) {  // empty sum: every output is +0
+        zero_acc();
+        for (int t = blockIdx.x; t < total; t += gridDim.x) {
+            int tm, tn;
+            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+            epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
+                        tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
+        }
+        return;
+    }
+
+    const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
+    uint32_t voff[T::LOADS];
+    int kc[T::LOADS];
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) {
+        const bool is_a = j < T::A_LOADS;
+        const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
+        const int row = g * T::ROWS_PER_LOAD + ld_r;
+        const int c = swz<T>(row, ld_p);
+        voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
+        kc[j] = c * 8;
+    }
+
+    int ld_tile = blockIdx.x, ld_ks = 0;
+    __amdgpu_buffer_rsrc_t ld_ra, ld_rb;
+    auto set_load_tile = [&](int t) {
+        if (t < total) {
+            int tm, tn;
+            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+            const int m0 = tm * T::BM, n0 = tn * T::BN;
+            ld_ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(T::BM, M - m0) * row_bytes);
+            ld_rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)min(T::BN, N - n0) * row_bytes);
+        } else {
+            ld_ra = make_rsrc(A, 0u);
+            ld_rb = make_rsrc(B, 0u);
+        }
+    };
+    auto advance_cursor = [&]() {
+        if (++ld_ks == nk) {
+            ld_ks = 0;
+            ld_tile += gridDim.x;
+            set_load_tile(ld_tile);
+        }
+    };
+    // loads j0 .. j0+3 of the cursor's step into `stage`
+    auto issue_loads4 = [&](int stage, int j0) {
+        const int k0 = ld_ks * T::BK;
+        const int krem = K - k0;
+        const uint32_t soff = (uint32_t)k0 * 2u;
+#pragma unroll
+        for (int j = j0; j < j0 + 4; ++j) {
+            const bool is_a = j < T::A_LOADS;
+            const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
+            unsigned char* dst = smem + stage * T::STAGE_BYTES + (is_a ? 0 : T::A_BYTES) + g * 1024;
+            const uint32_t v = kc[j] < krem ? voff[j] : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ld_ra : ld_rb, (lds_void_t*)dst, 16, v,
+                                                     soff, 0, 0);
+        }
+    };
+
+    // LDS byte address of this lane's fragment row, per operand and sub-step
+    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+    const uint32_t a_row_off = (uint32_t)((wm * T::WTM + fr_row) * T::ROW_BYTES);
+    const uint32_t b_row_off = (uint32_t)(T::A_BYTES + (wn * T::WTN + fr_row) * T::ROW_BYTES);
+    uint32_t fr_pos[T::KK];
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = (uint32_t)swz<T>(fr_row, 2 * kk + fr_hi) * 16u;
+
+    half8_t fa0[4], fb0[4], fa1[4], fb1[4];
+
+    set_load_tile(ld_tile);
+    issue_loads4(0, 0);
+    issue_loads4(0, 4);
+    issue_loads4(0, 8);
+    issue_loads4(0, 12);
+    advance_cursor();
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    issue_loads4(1, 0);
+    issue_loads4(1, 4);
+    issue_loads4(1, 8);
+    issue_loads4(1, 12);
+    advance_cursor();
+    read_frags_4x4(fa0, fb0, smem_base + a_row_off + fr_pos[0], smem_base + b_row_off + fr_pos[0]);
+
+    uint32_t cur = 0;  // stage of the step being computed
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        zero_acc();
+        for (int ks = 0; ks < nk; ++ks) {
+            const uint32_t sb = smem_base + cur * T::STAGE_BYTES;
+            const uint32_t nb = smem_base + (cur ^ 1u) * T::STAGE_BYTES;
+            substep_4x4(acc, fa0, fb0, fa1, fb1, sb + a_row_off + fr_pos[1], sb + b_row_off + fr_pos[1]);
+            substep_4x4(acc, fa1, fb1, fa0, fb0, sb + a_row_off + fr_pos[2], sb + b_row_off + fr_pos[2]);
+            substep_4x4(acc, fa0, fb0, fa1, fb1, sb + a_row_off + fr_pos[3], sb + b_row_off + fr_pos[3]);
+            // next step's stage landed (own loads) and visible (barrier);
+            // everyone is done with stage `cur`
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            read_frags_4x4(fa0, fb0, nb + a_row_off + fr_pos[0], nb + b_row_off + fr_pos[0]);
+            mfma_row_4<0>(acc, fa1[0], fb1);
+            issue_loads4((int)cur, 0);
+            mfma_row_4<1>(acc, fa1[1], fb1);
+            issue_loads4((int)cur, 4);
+            mfma_row_4<2>(acc, fa1[2], fb1);
+            issue_loads4((int)cur, 8);
+            mfma_row_4<3>(acc, fa1[3], fb1);
+            issue_loads4((int)cur, 12);
+            advance_cursor();
+            cur ^= 1u;
+        }
+        finish_mfma();
+        int tm, tn;
+        tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+        epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
+                    tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
+    }
+    // no global->LDS load or fragment read may still be in flight at the end
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+}
+
 // MFMA kernel with register-staged global loads.  Global data travels
 // global -> VGPRs -> LDS through two register sets and two LDS stages: the
 // tile of step s is loaded into a register set during step s - 3, written to
@@ -802,6 +1046,27 @@ int num_cus(int device)
     return n;
 }
 
+template <class T, bool ASM>
+int launch_persistent(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                      int group_m, hipStream_t stream)
+{
+    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
+    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) device = 0;
+    const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus(device));
+    const int c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
+    if (ASM)
+        hipLaunchKernelGGL((gemm_nt_f16_asm<T>), dim3((unsigned)grid), dim3(T::THREADS), 0, stream,
+                           (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N,
+                           (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
+    else
+        hipLaunchKernelGGL((gemm_nt_f16_stream<T>), dim3((unsigned)grid), dim3(T::THREADS), 0,
+                           stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M,
+                           (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
+    return (int)hipGetLastError();
+}
+
 template <class T>
 int launch_stream(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                   int group_m, hipStream_t stream)
@@ -840,6 +1105,7 @@ const Variant kVariants[] = {
     {"mfma32_256x256x64_w8_vgpr2", 256, 256, 8, launch_mfma_vgpr<T256_k64_s2_w8>},
     {"mfma32_256x256x64_w4_stream", 256, 256, 8, launch_stream<T256_k64_s2_w4>},
     {"mfma32_256x256x64_w8_stream", 256, 256, 8, launch_stream<T256_k64_s2_w8>},
+    {"mfma32_256x256x64_w4_asm", 256, 256, 8, launch_persistent<T256_k64_s2_w4, true>},
     {"simple_f32_per_element", 0, 0, 0, launch_simple},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
