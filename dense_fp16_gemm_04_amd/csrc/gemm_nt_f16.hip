@@ -799,6 +799,239 @@ gemm_nt_f16_asm(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
+// ---------------------------------------------------------------------------
+// Split-load hand-scheduled kernel (4 x 4 blocks per wave, any BK, STAGES >=
+// 3).  A sub-step's 16 MFMAs are issued as four rows of four; the first row
+// carries the 8 fragment reads of the next sub-step, and one global->LDS
+// load goes between consecutive rows.  The loads of step s are split: the
+// first four are issued right after the barrier that frees their stage
+// (after step s - STAGES), the rest between the rows of the following
+// step's first sub-steps.  Every load thus has STAGES - 2 full steps to
+// arrive, and the texture path sees a steady trickle instead of a burst.
+// ---------------------------------------------------------------------------
+// Row I of 4 MFMAs (acc[I][j] += B-frag j * A-frag), optionally waiting for
+// earlier fragment reads first and optionally reading the next sub-step's
+// fragments (A rows at pa + i * STRIDE, B rows at pb + j * STRIDE).
+template <int I, bool WAIT, int STRIDE>
+__device__ __forceinline__ void mma_row_reads(float16_t (&acc)[4][4], const half8_t& ca,
+                                              const half8_t (&cb)[4], half8_t (&na)[4],
+                                              half8_t (&nb)[4], uint32_t pa, uint32_t pb)
+{
+    if (WAIT) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile(
+        "v_mfma_f32_32x32x16_f16 %[c0], %[b0], %[a], %[c0]\n\t"
+        "ds_read_b128 %[na0], %[pa] offset:0\n\t"
+        "ds_read_b128 %[na1], %[pa] offset:%[s1]\n\t"
+        "v_mfma_f32_32x32x16_f16 %[c1], %[b1], %[a], %[c1]\n\t"
+        "ds_read_b128 %[na2], %[pa] offset:%[s2]\n\t"
+        "ds_read_b128 %[na3], %[pa] offset:%[s3]\n\t"
+        "v_mfma_f32_32x32x16_f16 %[c2], %[b2], %[a], %[c2]\n\t"
+        "ds_read_b128 %[nb0], %[pb] offset:0\n\t"
+        "ds_read_b128 %[nb1], %[pb] offset:%[s1]\n\t"
+        "v_mfma_f32_32x32x16_f16 %[c3], %[b3], %[a], %[c3]\n\t"
+        "ds_read_b128 %[nb2], %[pb] offset:%[s2]\n\t"
+        "ds_read_b128 %[nb3], %[pb] offset:%[s3]\n\t"
+        : [c0] "+a"(acc[I][0]), [c1] "+a"(acc[I][1]), [c2] "+a"(acc[I][2]), [c3] "+a"(acc[I][3]),
+          [na0] "=&v"(na[0]), [na1] "=&v"(na[1]), [na2] "=&v"(na[2]), [na3] "=&v"(na[3]),
+          [nb0] "=&v"(nb[0]), [nb1] "=&v"(nb[1]), [nb2] "=&v"(nb[2]), [nb3] "=&v"(nb[3])
+        : [a] "v"(ca), [b0] "v"(cb[0]), [b1] "v"(cb[1]), [b2] "v"(cb[2]), [b3] "v"(cb[3]),
+          [pa] "v"(pa), [pb] "v"(pb), [s1] "i"(STRIDE), [s2] "i"(2 * STRIDE), [s3] "i"(3 * STRIDE)
+        : "memory");
+}
+
+template <int BM_, int BN_, int BK_, int STAGES_>
+using Asm4x4 = TileShape<BM_, BN_, BK_, 2, 2, STAGES_, 1>;
+
+template <class T>
+__global__ void __launch_bounds__(T::THREADS, T::OCC)
+gemm_nt_f16_asm_split(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
+                      _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+                      int group_m, int c_vec)
+{
+    static_assert(T::FM == 4 && T::FN == 4 && T::WAVES == 4, "4 waves of 4 x 4 blocks");
+    static_assert(T::STAGES >= 3, "split loads need at least one step of slack");
+    constexpr int L = T::LOADS;              // global->LDS loads per wave per step
+    constexpr int FIRST = 4;                 // issued right after the barrier
+    constexpr int REST = L - FIRST;          // issued during the next step's sub-steps
+    constexpr int GAPS = (T::KK - 1) * 4;    // row gaps before the barrier
+    static_assert(REST <= GAPS, "every remaining load needs a row gap");
+    constexpr int WAIT_VM = (T::STAGES - 2) * L;
+    static_assert(WAIT_VM <= 63 && WAIT_VM + FIRST <= 63, "vmcnt holds at most 63");
+    constexpr int STRIDE = 32 * T::ROW_BYTES;  // bytes between 32-row fragment blocks
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+    const int total = tiles_m * tiles_n;
+    const int nk = (K + T::BK - 1) / T::BK;
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const int fr_row = lane & 31;
+    const int fr_hi = lane >> 5;
+
+    float16_t acc[4][4];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+    };
+
+    if (nk == 0) {  // empty sum: every output is +0
+        zero_acc();
+        for (int t = blockIdx.x; t < total; t += gridDim.x) {
+            int tm, tn;
+            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+            epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
+                        tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
+        }
+        return;
+    }
+
+    const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
+    uint32_t voff[L];
+    int kc[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const bool is_a = j < T::A_LOADS;
+        const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
+        const int row = g * T::ROWS_PER_LOAD + ld_r;
+        const int c = swz<T>(row, ld_p);
+        voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
+        kc[j] = c * 8;
+    }
+
+    int ld_tile = blockIdx.x, ld_ks = 0, ld_stage = 0;
+    __amdgpu_buffer_rsrc_t ld_ra, ld_rb;
+    auto set_load_tile = [&](int t) {
+        if (t < total) {
+            int tm, tn;
+            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+            const int m0 = tm * T::BM, n0 = tn * T::BN;
+            ld_ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(T::BM, M - m0) * row_bytes);
+            ld_rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)min(T::BN, N - n0) * row_bytes);
+        } else {
+            ld_ra = make_rsrc(A, 0u);
+            ld_rb = make_rsrc(B, 0u);
+        }
+    };
+    auto advance_cursor = [&]() {
+        ld_stage = ld_stage + 1 == T::STAGES ? 0 : ld_stage + 1;
+        if (++ld_ks == nk) {
+            ld_ks = 0;
+            ld_tile += gridDim.x;
+            set_load_tile(ld_tile);
+        }
+    };
+    // load j of the cursor's step into the cursor's stage
+    auto load_one = [&](int j) {
+        const int k0 = ld_ks * T::BK;
+        const bool is_a = j < T::A_LOADS;
+        const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
+        unsigned char* dst = smem + ld_stage * T::STAGE_BYTES + (is_a ? 0 : T::A_BYTES) + g * 1024;
+        const uint32_t v = kc[j] < K - k0 ? voff[j] : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ld_ra : ld_rb, (lds_void_t*)dst, 16, v,
+                                                 (uint32_t)k0 * 2u, 0, 0);
+    };
+
+    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+    const uint32_t a_row_off = (uint32_t)((wm * T::WTM + fr_row) * T::ROW_BYTES);
+    const uint32_t b_row_off = (uint32_t)(T::A_BYTES + (wn * T::WTN + fr_row) * T::ROW_BYTES);
+    uint32_t fr_pos[T::KK];
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = (uint32_t)swz<T>(fr_row, 2 * kk + fr_hi) * 16u;
+
+    half8_t fa[2][4], fb[2][4];
+
+    // Prologue: steps 0 .. STAGES-2 whole, the first loads of step STAGES-1.
+    set_load_tile(ld_tile);
+    for (int s = 0; s < T::STAGES - 1; ++s) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) load_one(j);
+        advance_cursor();
+    }
+#pragma unroll
+    for (int j = 0; j < FIRST; ++j) load_one(j);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_VM + FIRST));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // fragments of step 0, sub-step 0
+    asm volatile(
+        "ds_read_b128 %[a0], %[pa] offset:0\n\tds_read_b128 %[a1], %[pa] offset:%[s1]\n\t"
+        "ds_read_b128 %[a2], %[pa] offset:%[s2]\n\tds_read_b128 %[a3], %[pa] offset:%[s3]\n\t"
+        "ds_read_b128 %[b0], %[pb] offset:0\n\tds_read_b128 %[b1], %[pb] offset:%[s1]\n\t"
+        "ds_read_b128 %[b2], %[pb] offset:%[s2]\n\tds_read_b128 %[b3], %[pb] offset:%[s3]\n\t"
+        : [a0] "=&v"(fa[0][0]), [a1] "=&v"(fa[0][1]), [a2] "=&v"(fa[0][2]), [a3] "=&v"(fa[0][3]),
+          [b0] "=&v"(fb[0][0]), [b1] "=&v"(fb[0][1]), [b2] "=&v"(fb[0][2]), [b3] "=&v"(fb[0][3])
+        : [pa] "v"(smem_base + a_row_off + fr_pos[0]), [pb] "v"(smem_base + b_row_off + fr_pos[0]),
+          [s1] "i"(STRIDE), [s2] "i"(2 * STRIDE), [s3] "i"(3 * STRIDE)
+        : "memory");
+
+    int cur = 0;  // stage of the step being computed
+    bool after_epilogue = false;
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        zero_acc();
+        for (int ks = 0; ks < nk; ++ks) {
+            const uint32_t sb = smem_base + (uint32_t)(cur * T::STAGE_BYTES);
+            const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
+            const uint32_t nb = smem_base + (uint32_t)(nxt * T::STAGE_BYTES);
+            // sub-steps 0 .. KK-2; the remaining loads of the cursor's step
+            // go into the row gaps
+#pragma unroll
+            for (int kk = 0; kk + 1 < T::KK; ++kk) {
+                const int cb_ = kk & 1, nb_ = (kk + 1) & 1;
+                const uint32_t pa = sb + a_row_off + fr_pos[kk + 1];
+                const uint32_t pb = sb + b_row_off + fr_pos[kk + 1];
+                mma_row_reads<0, true, STRIDE>(acc, fa[cb_][0], fb[cb_], fa[nb_], fb[nb_], pa, pb);
+                if (kk * 4 + 0 < REST) load_one(FIRST + kk * 4 + 0);
+                mfma_row_4<1>(acc, fa[cb_][1], fb[cb_]);
+                if (kk * 4 + 1 < REST) load_one(FIRST + kk * 4 + 1);
+                mfma_row_4<2>(acc, fa[cb_][2], fb[cb_]);
+                if (kk * 4 + 2 < REST) load_one(FIRST + kk * 4 + 2);
+                mfma_row_4<3>(acc, fa[cb_][3], fb[cb_]);
+                if (kk * 4 + 3 < REST) load_one(FIRST + kk * 4 + 3);
+            }
+            advance_cursor();
+            // step ks + 1 has landed and is visible; stage `cur` is free.
+            // After an epilogue its stores are outstanding too: wait for all.
+            if (after_epilogue)
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%[n]) lgkmcnt(0)\n\ts_barrier" ::
+                                 [n] "i"(WAIT_VM) : "memory");
+            after_epilogue = false;
+            // last sub-step, with the next step's first fragments and the
+            // first loads of the cursor's step (into stage `cur`)
+            {
+                constexpr int cb_ = (T::KK - 1) & 1;
+                const uint32_t pa = nb + a_row_off + fr_pos[0];
+                const uint32_t pb = nb + b_row_off + fr_pos[0];
+                mma_row_reads<0, false, STRIDE>(acc, fa[cb_][0], fb[cb_], fa[0], fb[0], pa, pb);
+                load_one(0);
+                mfma_row_4<1>(acc, fa[cb_][1], fb[cb_]);
+                load_one(1);
+                mfma_row_4<2>(acc, fa[cb_][2], fb[cb_]);
+                load_one(2);
+                mfma_row_4<3>(acc, fa[cb_][3], fb[cb_]);
+                load_one(3);
+            }
+            cur = nxt;
+        }
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        int tm, tn;
+        tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+        epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
+                    tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
+        after_epilogue = true;
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+}
+
 // MFMA kernel with register-staged global loads.  Global data travels
 // global -> VGPRs -> LDS through two register sets and two LDS stages: the
 // tile of step s is loaded into a register set during step s - 3, written to
@@ -1046,6 +1279,22 @@ int num_cus(int device)
     return n;
 }
 
+template <class T>
+int launch_asm_split(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                     int group_m, hipStream_t stream)
+{
+    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
+    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) device = 0;
+    const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus(device));
+    const int c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
+    hipLaunchKernelGGL((gemm_nt_f16_asm_split<T>), dim3((unsigned)grid), dim3(T::THREADS), 0,
+                       stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M,
+                       (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
+    return (int)hipGetLastError();
+}
+
 template <class T, bool ASM>
 int launch_persistent(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                       int group_m, hipStream_t stream)
@@ -1106,6 +1355,8 @@ const Variant kVariants[] = {
     {"mfma32_256x256x64_w4_stream", 256, 256, 8, launch_stream<T256_k64_s2_w4>},
     {"mfma32_256x256x64_w8_stream", 256, 256, 8, launch_stream<T256_k64_s2_w8>},
     {"mfma32_256x256x64_w4_asm", 256, 256, 8, launch_persistent<T256_k64_s2_w4, true>},
+    {"mfma32_256x256x32_w4_s4_asm", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 32, 4>>},
+    {"mfma32_256x256x32_w4_s5_asm", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 32, 5>>},
     {"simple_f32_per_element", 0, 0, 0, launch_simple},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
