@@ -800,8 +800,8 @@ gemm_nt_f16_asm(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
-// Split-load hand-scheduled kernel (4 x 4 blocks per wave, any BK, STAGES >=
-// 3).  A sub-step's 16 MFMAs are issued as four rows of four; the first row
+// Split-load hand-scheduled kernel (4 x 4 blocks per wave, any BK and
+// STAGES).  A sub-step's 16 MFMAs are issued as four rows of four; the first row
 // carries the 8 fragment reads of the next sub-step, and one global->LDS
 // load goes between consecutive rows.  The loads of step s are split: the
 // first four are issued right after the barrier that frees their stage
@@ -849,7 +849,7 @@ gemm_nt_f16_asm_split(const _Float16* __restrict__ A, const _Float16* __restrict
                       int group_m, int c_vec)
 {
     static_assert(T::FM == 4 && T::FN == 4 && T::WAVES == 4, "4 waves of 4 x 4 blocks");
-    static_assert(T::STAGES >= 3, "split loads need at least one step of slack");
+    static_assert(T::STAGES >= 2, "a two-stage ring at least");
     constexpr int L = T::LOADS;              // global->LDS loads per wave per step
     constexpr int FIRST = 4;                 // issued right after the barrier
     constexpr int REST = L - FIRST;          // issued during the next step's sub-steps
@@ -1355,6 +1355,7 @@ const Variant kVariants[] = {
     {"mfma32_256x256x64_w4_stream", 256, 256, 8, launch_stream<T256_k64_s2_w4>},
     {"mfma32_256x256x64_w8_stream", 256, 256, 8, launch_stream<T256_k64_s2_w8>},
     {"mfma32_256x256x64_w4_asm", 256, 256, 8, launch_persistent<T256_k64_s2_w4, true>},
+    {"mfma32_256x256x64_w4_s2_split", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 64, 2>>},
     {"mfma32_256x256x32_w4_s4_asm", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 32, 4>>},
     {"mfma32_256x256x32_w4_s5_asm", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 32, 5>>},
     {"simple_f32_per_element", 0, 0, 0, launch_simple},
