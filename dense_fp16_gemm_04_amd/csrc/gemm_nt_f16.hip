@@ -4,33 +4,36 @@
 // section "Block Tiling" (A is M x K, B is N x K, both K-major, C is M x N)
 // with fp32 accumulation ("Data Flow") and one fp16 cast after the K loop
 // ("Walkthrough" / "Epilogue").  The pages build this for Hopper out of TMA,
-// mbarriers and warp-group MMA; none of those exist on CDNA4, so the kernel
-// keeps only the ideas that still hold and re-derives the rest for gfx950:
+// mbarriers and warp-group MMA; none of those exist on CDNA4, so the kernels
+// keep only the ideas that still hold and re-derive the rest for gfx950:
 //
-//  * one workgroup per BM x BN output tile, K walked in BK = 64 steps
+//  * one workgroup per BM x BN output tile, K walked in BK-deep steps
 //    ("0. A Minimal Hopper Matmul", "Block Tiling");
-//  * a multi-stage shared-memory ring so loads of step k+1 overlap the
-//    matrix-core work of step k ("3. Warp Specialization", introduction and
-//    "Draining the Pipeline").  On CDNA4 every wave issues its own loads, so
-//    there is no producer warp; loads go straight from global memory to LDS
-//    (buffer_load ... lds), completion is tracked with the vmcnt counter and
-//    made visible to the other waves with one s_barrier per K step;
+//  * a multi-stage shared-memory ring so loads of later steps overlap the
+//    matrix-core work of the current one ("3. Warp Specialization",
+//    introduction and "Draining the Pipeline").  On CDNA4 every wave issues
+//    its own loads, so there is no producer warp: loads go straight from
+//    global memory to LDS (buffer_load ... lds), completion is tracked with
+//    the vmcnt counter and made visible to the other waves with one
+//    s_barrier per K step;
 //  * several waves per workgroup, each owning a sub-tile of C and sharing the
-//    B tile in LDS ("6. Four Consumers, FP16 Accumulation, and a TMA
+//    operand tiles in LDS ("6. Four Consumers, FP16 Accumulation, and a TMA
 //    Epilogue", introduction);
 //  * a grouped raster of tiles for cache reuse ("6. Four Consumers ...",
 //    "What Changed from V5", raster group width), here additionally made
 //    aware of the 8 XCDs, each with its own L2;
 //  * an fp32 accumulator sized to the register file ("6. Four Consumers ...",
-//    "The Register Budget Problem"): on CDNA4 the MFMA accumulates in fp32 in
-//    the 256 accumulation registers (AGPRs) per lane, so a 4-wave 256 x 256
-//    tile gives each wave a 128 x 128 fp32 accumulator = 256 AGPRs.
+//    "The Register Budget Problem"): the MFMA accumulates in fp32, and a
+//    256 x 256 tile needs 256 KiB of accumulators: 4 waves x 256 AGPRs per
+//    lane (one wave per SIMD), or 8 waves x 128 (two per SIMD).
 //
 // LDS layout of one stage: the A tile (BM rows) then the B tile (BN rows);
-// each row is BK = 64 fp16 = 128 bytes = 8 chunks of 16 bytes.  Chunk c of
-// row r is stored at chunk position c ^ (r & 7), so the 16-byte fragment
-// reads of 8 consecutive rows at the same logical chunk land in 8 different
-// positions of the row (different LDS banks).
+// each row holds BK fp16 (64 or 128 bytes) as 16-byte chunks.  gfx950's LDS
+// serves 64 banks x 4 bytes per cycle, so the 16 lanes of a 16-byte read
+// must hit 16 different 16-byte bank groups: chunk c of row r is stored at
+// position c ^ ((r / ROWS_PER_LINE) % CHUNKS), ROWS_PER_LINE being the rows
+// that share one 256-byte line.  Reads of 16 consecutive rows at one logical
+// chunk are then conflict-free (measured: zero bank conflicts).
 //
 // Matrix-core step: v_mfma_f32_32x32x16_f16.  Operand lane l holds 8
 // consecutive-k fp16 values of row (l % 32), k offset 8 * (l / 32); the same
@@ -54,7 +57,6 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -1032,174 +1034,6 @@ gemm_nt_f16_asm_split(const _Float16* __restrict__ A, const _Float16* __restrict
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
-// MFMA kernel with register-staged global loads.  Global data travels
-// global -> VGPRs -> LDS through two register sets and two LDS stages: the
-// tile of step s is loaded into a register set during step s - 3, written to
-// LDS stage s % 2 during step s - 1 and read during step s.  Loads therefore
-// have two steps of matrix-core time to arrive (a direct-to-LDS load into a
-// two-stage ring has one), and the per-step barrier never waits on global
-// memory, only on this step's LDS traffic.
-//
-// Step ks (LDS stage p = ks & 1):
-//   region 1  MFMA sub-steps 0 .. KK-2 of step ks, fragment reads one
-//             sub-step ahead; interleaved with them, the LDS writes of step
-//             ks+1 (register set p^1 -> stage p^1) each followed by the
-//             global load of step ks+3 into the register it just freed;
-//   barrier   (this wave's LDS reads and writes complete): every wave is done
-//             reading stage p, and step ks+1 is visible in stage p^1;
-//   region 2  fragment reads of step ks+1 sub-step 0, then the MFMAs of
-//             sub-step KK-1 of step ks.
-// Steps past the end of K load zeros, so the loop runs an even number of
-// steps (a zero step adds nothing) and needs no tail code.
-template <class T>
-__global__ void __launch_bounds__(T::THREADS, T::OCC)
-gemm_nt_f16_mfma_vgpr(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
-                      _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
-                      int group_m, int c_vec)
-{
-    static_assert(T::STAGES == 2, "two LDS stages, two register sets");
-    constexpr int WPS = (T::LOADS + T::KK - 2) / (T::KK - 1);  // LDS writes per sub-step
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
-
-    int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * T::BM, n0 = tn * T::BN;
-    const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);
-    const uint32_t row_bytes = (uint32_t)K * 2u;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * row_bytes);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * row_bytes);
-
-    // Load j of this wave covers tile bytes [g * 1024, g * 1024 + 1024),
-    // g = wave * A_LOADS + j for A (j < A_LOADS), likewise for B:
-    // ROWS_PER_LOAD whole rows, lane l reading logical chunk l % CHUNKS of
-    // row g * ROWS_PER_LOAD + l / CHUNKS (coalesced) and writing it at its
-    // swizzled LDS position.  A row offset stays below 2^31 (K < 2^22, rows
-    // < 256), so adding 2^31 pushes a load past any buffer: it reads zero.
-    const int ld_r = lane / T::CHUNKS, ld_c = lane % T::CHUNKS;
-    const int ld_kc = ld_c * 8;
-    uint32_t voff[T::LOADS];
-    int lds_off[T::LOADS];
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) {
-        const bool is_a = j < T::A_LOADS;
-        const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
-        const int row = g * T::ROWS_PER_LOAD + ld_r;
-        voff[j] = (uint32_t)row * row_bytes + (uint32_t)ld_c * 16u;
-        lds_off[j] = (is_a ? 0 : T::A_BYTES) + row * T::ROW_BYTES + swz<T>(row, ld_c) * 16;
-    }
-
-    u32x4_t regs[2][T::LOADS];
-    auto gload_one = [&](u32x4_t (&dst)[T::LOADS], int j, int kstep) {
-        const int k0 = kstep * T::BK;
-        const uint32_t oob = ld_kc < K - k0 ? 0u : kOob;  // K tail and steps past K read zero
-        dst[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 j < T::A_LOADS ? ra : rb, (int)(voff[j] + oob), k0 * 2, 0));
-    };
-    auto lstore_one = [&](const u32x4_t (&src)[T::LOADS], int j, int stage) {
-        *(u32x4_t*)(smem + stage * T::STAGE_BYTES + lds_off[j]) = src[j];
-    };
-
-    const int fr_row = lane & 31;
-    const int fr_hi = lane >> 5;
-    const int a_row0 = wm * T::WTM + fr_row;
-    const int b_row0 = wn * T::WTN + fr_row;
-    int fr_pos[T::KK];
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, 2 * kk + fr_hi) * 16;
-
-    half8_t fa[2][T::FM], fb[2][T::FN];
-    float16_t acc[T::FM][T::FN];
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    auto read_frags = [&](int buf, int stage, int kk) {
-        const unsigned char* base = smem + stage * T::STAGE_BYTES;
-        const unsigned char* pa = base + a_row0 * T::ROW_BYTES + fr_pos[kk];
-        const unsigned char* pb = base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[kk];
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i) fa[buf][i] = *(const half8_t*)(pa + i * 32 * T::ROW_BYTES);
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) fb[buf][j] = *(const half8_t*)(pb + j * 32 * T::ROW_BYTES);
-    };
-    auto mma = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[buf][j], fa[buf][i], acc[i][j],
-                                                                   0, 0, 0);
-    };
-    // Workgroup barrier that orders LDS traffic only: this wave's LDS reads
-    // and writes are complete, global loads may stay in flight.
-    auto lds_barrier = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    const int nk = (K + T::BK - 1) / T::BK;
-    const int nk2 = (nk + 1) & ~1;
-
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) gload_one(regs[0], j, 0);
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) gload_one(regs[1], j, 1);
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) lstore_one(regs[0], j, 0);
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) gload_one(regs[0], j, 2);
-    lds_barrier();
-    read_frags(0, 0, 0);
-
-    auto step = [&](int ks, int p) {
-#pragma unroll
-        for (int kk = 0; kk + 1 < T::KK; ++kk) {
-            read_frags((kk + 1) & 1, p, kk + 1);
-            mma(kk & 1);
-#pragma unroll
-            for (int w = 0; w < WPS; ++w) {
-                const int j = kk * WPS + w;
-                if (j < T::LOADS) {
-                    lstore_one(regs[p ^ 1], j, p ^ 1);
-                    gload_one(regs[p ^ 1], j, ks + 3);
-                }
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk + 1 < T::KK; ++kk) {
-            __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
-#pragma unroll
-            for (int i = 0; i < T::FM * T::FN; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-                if (i < WPS && kk * WPS + i < T::LOADS) {
-                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // one LDS write
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // one global load
-                }
-            }
-        }
-        lds_barrier();
-        read_frags(T::KK & 1, p ^ 1, 0);
-        mma((T::KK - 1) & 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);      // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, T::FM * T::FN, 1);      // MFMAs
-    };
-    for (int ks = 0; ks < nk2; ks += 2) {
-        step(ks, 0);
-        step(ks + 1, 1);
-    }
-
-    epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
-}
-
 // Plain per-element kernel for inputs the MFMA kernels do not take
 // (unaligned pointers, K % 8 != 0, very long K).  One thread per output,
 // fp32 accumulation in k order, one fp16 rounding at the end.
@@ -1222,7 +1056,6 @@ gemm_nt_f16_simple(const _Float16* __restrict__ A, const _Float16* __restrict__ 
 //                  BM   BN   BK  WM  WN  S  OCC
 typedef TileShape<256, 256, 64, 2, 2, 2, 1> T256_k64_s2_w4;
 typedef TileShape<256, 256, 32, 2, 2, 4, 1> T256_k32_s4_w4;
-typedef TileShape<256, 256, 32, 2, 4, 4, 2> T256_k32_s4_w8;
 typedef TileShape<256, 256, 64, 2, 4, 2, 2> T256_k64_s2_w8;
 typedef TileShape<256, 128, 64, 2, 2, 3, 1> T256x128_k64_s3_w4;
 typedef TileShape<128, 128, 64, 2, 2, 3, 1> T128_k64_s3_w4;
@@ -1248,20 +1081,6 @@ int launch_mfma(const void* A, const void* B, void* C, int64_t M, int64_t N, int
     hipLaunchKernelGGL((gemm_nt_f16_mfma<T>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS),
                        0, stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M,
                        (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
-    return (int)hipGetLastError();
-}
-
-template <class T>
-int launch_mfma_vgpr(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                     int group_m, hipStream_t stream)
-{
-    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
-    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
-    const int c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
-    hipLaunchKernelGGL((gemm_nt_f16_mfma_vgpr<T>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(T::THREADS), 0, stream, (const _Float16*)A, (const _Float16*)B,
-                       (_Float16*)C, (int)M, (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m,
-                       c_vec);
     return (int)hipGetLastError();
 }
 
@@ -1342,22 +1161,19 @@ int launch_simple(const void* A, const void* B, void* C, int64_t M, int64_t N, i
     return (int)hipGetLastError();
 }
 
+// Variant 0 is the default for large problems; the others are kept for
+// smaller shapes and as the measured alternatives (tile shape, ring depth,
+// persistence, hand-scheduled issue order).
 const Variant kVariants[] = {
-    {"mfma32_256x256x32_w4_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w4>},
-    {"mfma32_256x256x32_w8_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w8>},
-    {"mfma32_256x256x64_w4_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w4>},
     {"mfma32_256x256x64_w8_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8>},
+    {"mfma32_256x256x64_w4_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w4>},
+    {"mfma32_256x256x32_w4_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w4>},
     {"mfma32_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4>},
     {"mfma32_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4>},
     {"mfma32_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4>},
-    {"mfma32_256x256x64_w4_vgpr2", 256, 256, 8, launch_mfma_vgpr<T256_k64_s2_w4>},
-    {"mfma32_256x256x64_w8_vgpr2", 256, 256, 8, launch_mfma_vgpr<T256_k64_s2_w8>},
     {"mfma32_256x256x64_w4_stream", 256, 256, 8, launch_stream<T256_k64_s2_w4>},
-    {"mfma32_256x256x64_w8_stream", 256, 256, 8, launch_stream<T256_k64_s2_w8>},
     {"mfma32_256x256x64_w4_asm", 256, 256, 8, launch_persistent<T256_k64_s2_w4, true>},
-    {"mfma32_256x256x64_w4_s2_split", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 64, 2>>},
-    {"mfma32_256x256x32_w4_s4_asm", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 32, 4>>},
-    {"mfma32_256x256x32_w4_s5_asm", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 32, 5>>},
+    {"mfma32_256x256x32_w4_s5_split", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 32, 5>>},
     {"simple_f32_per_element", 0, 0, 0, launch_simple},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -1397,11 +1213,10 @@ int select_mfma(int64_t M, int64_t N)
 {
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    if (t256 >= 192) return 0;
-    if (t128 >= 128) return 5;
-    return 6;
+    if (t256 >= 192) return 0;  // 8-wave 256 x 256
+    if (t128 >= 192) return 4;  // 128 x 128
+    return 5;                   // 64 x 64
 }
-
 }  // namespace
 
 extern "C" {
