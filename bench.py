@@ -28,10 +28,11 @@ if ROOT not in sys.path:
 METRIC = "TFLOP/s fp16 GEMM C=A·Bᵀ at M=N=K=8192; % of MI355X dense fp16 MFMA peak"
 # 256 CUs x 4096 dense fp16 flop per clock per CU x 2.4 GHz (AMD's 2.5 PFLOP/s)
 PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
-# HBM byte counts measured with rocprofv3 (FETCH_SIZE / WRITE_SIZE, scaled by
-# the same counters on a plain copy kernel) for the current 8192^3 kernel;
-# None until taken for this kernel version.
-TRAFFIC_BYTES = None
+# HBM bytes per launch measured with rocprofv3 (FETCH_SIZE x 2.000 plus
+# WRITE_SIZE x 1.000, the factors read off a plain 1 GiB device copy) for one
+# kernel on one workload.  Reported only for that pair; reset to None when the
+# kernel changes.
+TRAFFIC = {"workload": "square_8192", "kernel": "mfma32_256x256x64_w8_s2", "bytes": 1.876e9}
 
 
 def log(*a):
@@ -159,7 +160,8 @@ def main(argv=None) -> int:
         "peak": PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": tflops / PEAK_TFLOPS,
-        "traffic": TRAFFIC_BYTES if (TRAFFIC_BYTES and w is workloads.HEADLINE) else None,
+        "traffic": (TRAFFIC["bytes"] if TRAFFIC and TRAFFIC["workload"] == w.name
+                    and TRAFFIC["kernel"] == vname else None),
     }
     rec = {
         "metric": METRIC,
