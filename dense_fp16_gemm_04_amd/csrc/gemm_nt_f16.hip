@@ -71,6 +71,19 @@ constexpr int kRsrcWord3 = 0x00020000;
 // expcnt[6:4], lgkmcnt[11:8]); the counters not waited on are left at max.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Wait until at most VM of this wave's global->LDS loads are still in flight
+// and all of its LDS reads have returned, then meet the other waves at the
+// barrier.  Written as one asm statement with a memory clobber so no LDS
+// access moves across it.  (__syncthreads() would add a workgroup fence,
+// which waits for every outstanding load, vmcnt(0), and so would cap the
+// ring at two stages whatever its depth.)
+template <int VM>
+__device__ __forceinline__ void lds_barrier()
+{
+    static_assert(VM >= 0 && VM <= 63, "vmcnt holds 0 .. 63");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(VM) : "memory");
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
@@ -106,7 +119,15 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
 //   STAGES    depth of the LDS ring: loads run STAGES - 1 steps ahead
 //   MIN_WAVES_PER_SIMD  occupancy hint (1: up to 512 registers per lane, the
 //             256 AGPRs holding the accumulator; 2: up to 256)
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_>
+//   EARLY     how many of a loading wave's global->LDS loads of a step are
+//             issued one step sooner, spread over the MFMAs before the
+//             barrier (needs STAGES >= 3); the others go out right after it
+//   LOADERS   how many waves issue the global->LDS loads (0: all of them);
+//             with half of the waves loading, each SIMD runs one wave that
+//             never waits on the vector memory queue and keeps the matrix
+//             core busy while its partner issues loads
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_, int EARLY_ = 0,
+          int LOADERS_ = 0>
 struct TileShape {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -129,16 +150,39 @@ struct TileShape {
     static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;         // 1 KiB per wave load
-    static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
-    static constexpr int LOADS = A_LOADS + B_LOADS;                // per wave per step
+    static constexpr int LOADERS = LOADERS_ == 0 ? WAVES : LOADERS_;
+    static constexpr int A_LOADS = A_BYTES / 1024 / LOADERS;       // 1 KiB per wave load
+    static constexpr int B_LOADS = B_BYTES / 1024 / LOADERS;
+    static constexpr int LOADS = A_LOADS + B_LOADS;                // per loading wave per step
+    static constexpr int EARLY = EARLY_, LATE = LOADS - EARLY_;
+    static constexpr int R1_MFMAS = (KK - 1) * FM * FN;           // MFMAs before the barrier
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(ROWS_PER_LINE * CHUNKS == 16, "swizzle covers 16 lanes");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(A_LOADS * WAVES * 1024 == A_BYTES, "A tile must split evenly over waves");
-    static_assert(B_LOADS * WAVES * 1024 == B_BYTES, "B tile must split evenly over waves");
+    static_assert(LOADERS >= 1 && LOADERS <= WAVES, "loading waves are a subset of the waves");
+    static_assert(A_LOADS * LOADERS * 1024 == A_BYTES, "A tile must split evenly over loading waves");
+    static_assert(B_LOADS * LOADERS * 1024 == B_BYTES, "B tile must split evenly over loading waves");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
     static_assert(STAGES >= 2 && LOADS * (STAGES - 2) <= 63, "vmcnt holds at most 63");
+    static_assert(EARLY >= 0 && EARLY <= LOADS && (EARLY == 0 || STAGES >= 3),
+                  "early loads need a free stage one step ahead");
+    static_assert(EARLY <= 4 * R1_MFMAS && LATE <= 4 * FM * FN, "at most 4 loads per MFMA");
+};
+
+// Scheduling group of n (0 .. 4, known after unrolling) vector memory
+// instructions in sync group G.
+template <int G>
+__device__ __forceinline__ void sched_vmem(int n)
+{
+    if (n == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, G);
+    else if (n == 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, G);
+    else if (n == 3) __builtin_amdgcn_sched_group_barrier(0x020, 3, G);
+    else if (n == 4) __builtin_amdgcn_sched_group_barrier(0x020, 4, G);
+}
+
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
 };
 
 template <class T>
@@ -210,51 +254,58 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * row_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * row_bytes);
 
-    // Global->LDS copy assignment.  Load j of this wave fills bytes
+    // Global->LDS copy assignment.  Load j of loading wave w fills bytes
     // [g * 1024, g * 1024 + 1024) of the operand's tile in the stage,
-    // g = wave * LOADS + j, i.e. ROWS_PER_LOAD whole rows; lane l writes
+    // g = w * LOADS + j, i.e. ROWS_PER_LOAD whole rows; lane l writes
     // position l % CHUNKS of row g * ROWS_PER_LOAD + l / CHUNKS, so it
     // fetches the logical chunk that the swizzle puts at that position.
+    // Waves 0 .. LOADERS-1 load (waves are dealt to the four SIMDs in turn,
+    // so with LOADERS = WAVES / 2 every SIMD hosts one loading wave).
+    const bool loader = wave < T::LOADERS;
+    const int lw = loader ? wave : 0;
     const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
     uint32_t a_voff[T::A_LOADS], b_voff[T::B_LOADS];
     int a_kc[T::A_LOADS], b_kc[T::B_LOADS];  // first k of the fetched chunk
 #pragma unroll
     for (int j = 0; j < T::A_LOADS; ++j) {
-        const int row = (wave * T::A_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
+        const int row = (lw * T::A_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
         const int c = swz<T>(row, ld_p);
         a_voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
         a_kc[j] = c * 8;
     }
 #pragma unroll
     for (int j = 0; j < T::B_LOADS; ++j) {
-        const int row = (wave * T::B_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
+        const int row = (lw * T::B_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
         const int c = swz<T>(row, ld_p);
         b_voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
         b_kc[j] = c * 8;
     }
 
-    // Issues the loads of step `kstep` into `stage`.  Steps past the end of
-    // K load zeros (every chunk is out of range), so the ring can run without
-    // branches; those stages are never read.
-    auto issue_loads = [&](int stage, int kstep) {
+    // Issues loads [first, first + count) of step `kstep` into `stage`
+    // (A's loads first, then B's).  Steps past the end of K load zeros (every
+    // chunk is out of range), so the ring can run without branches; those
+    // stages are never read.
+    auto issue_load_range = [&](int stage, int kstep, int first, int count) {
         const int k0 = kstep * T::BK;
         const int krem = K - k0;  // chunks starting at or past K read as zero
         const uint32_t soff = (uint32_t)k0 * 2u;
-        unsigned char* a_dst = smem + stage * T::STAGE_BYTES + wave * T::A_LOADS * 1024;
-        unsigned char* b_dst = smem + stage * T::STAGE_BYTES + T::A_BYTES + wave * T::B_LOADS * 1024;
+        unsigned char* a_dst = smem + stage * T::STAGE_BYTES + lw * T::A_LOADS * 1024;
+        unsigned char* b_dst = smem + stage * T::STAGE_BYTES + T::A_BYTES + lw * T::B_LOADS * 1024;
 #pragma unroll
-        for (int j = 0; j < T::A_LOADS; ++j) {
-            const uint32_t v = a_kc[j] < krem ? a_voff[j] : kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(a_dst + j * 1024), 16, v, soff,
-                                                     0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < T::B_LOADS; ++j) {
-            const uint32_t v = b_kc[j] < krem ? b_voff[j] : kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(b_dst + j * 1024), 16, v, soff,
-                                                     0, 0);
+        for (int l = first; l < first + count; ++l) {
+            if (l < T::A_LOADS) {
+                const uint32_t v = a_kc[l] < krem ? a_voff[l] : kOob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(a_dst + l * 1024), 16, v, soff,
+                                                         0, 0);
+            } else {
+                const int j = l - T::A_LOADS;
+                const uint32_t v = b_kc[j] < krem ? b_voff[j] : kOob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(b_dst + j * 1024), 16, v, soff,
+                                                         0, 0);
+            }
         }
     };
+    auto issue_loads = [&](int stage, int kstep) { issue_load_range(stage, kstep, 0, T::LOADS); };
 
     // Fragment reads: row (l % 32) of each 32-row block, logical chunk
     // 2 * kk + l / 32 for k sub-step kk (16 k values per MFMA).  Row offsets
@@ -312,43 +363,72 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     //   after the barrier:    fragment reads of the next step's sub-step 0,
     //                         then the MFMAs of sub-step KK-1, each followed
     //                         by one of the wave's global->LDS loads.
-    if (nk > 0) {
+    //
+    // With EARLY > 0 a step's loads go out in two parts: the first LATE right
+    // after the barrier that frees their stage, the last EARLY during the
+    // next step's MFMAs before its barrier, one every R1_MFMAS / EARLY MFMAs.
+    // Spreading them keeps the vector memory unit's queue short, so a load
+    // waiting for a queue slot does not hold up the MFMAs behind it.  Loads
+    // leave in the same order either way, so the vmcnt count at each barrier
+    // is unchanged: only the STAGES - 2 steps after the next one may be in
+    // flight.
+    // The loop is compiled twice: for loading waves and, when only some
+    // waves load, for the others (no loads, and nothing in flight at the
+    // barriers).
+    auto main_loop = [&](auto tag) {
+        constexpr bool LD = decltype(tag)::value;
 #pragma unroll
-        for (int s = 0; s < T::STAGES - 1; ++s) issue_loads(s, s);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::LOADS * (T::STAGES - 2)));
-        __syncthreads();
-        issue_loads(T::STAGES - 1, T::STAGES - 1);
+        for (int s = 0; s < T::STAGES - 1; ++s)
+            if constexpr (LD) issue_loads(s, s);
+        lds_barrier<T::LOADS * (T::STAGES - 2)>();
+        if constexpr (LD) issue_load_range(T::STAGES - 1, T::STAGES - 1, 0, T::LATE);
         read_frags(0, smem, 0);
 
         int cur = 0;  // stage of step ks
         for (int ks = 0; ks < nk; ++ks) {
             const unsigned char* base = smem + cur * T::STAGE_BYTES;
             const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
+            const int prv = cur == 0 ? T::STAGES - 1 : cur - 1;  // free since the last barrier
 #pragma unroll
             for (int kk = 0; kk + 1 < T::KK; ++kk) {
                 read_frags((kk + 1) & 1, base, kk + 1);
                 mma(kk & 1);
             }
+            if constexpr (LD && T::EARLY > 0) issue_load_range(prv, ks + T::STAGES - 1, T::LATE, T::EARLY);
 #pragma unroll
             for (int kk = 0; kk + 1 < T::KK; ++kk) {
                 __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
-                __builtin_amdgcn_sched_group_barrier(0x008, T::FM * T::FN, 0);  // MFMAs
+#pragma unroll
+                for (int i = 0; i < T::FM * T::FN; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+                    constexpr int E = LD ? T::EARLY : 0;
+                    const int n = kk * T::FM * T::FN + i;
+                    const int nl = E * (n + 1) / T::R1_MFMAS - E * n / T::R1_MFMAS;
+                    sched_vmem<0>(nl);                                          // loads
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::LOADS * (T::STAGES - 2)));
-            __syncthreads();
+            lds_barrier<T::LOADS * (T::STAGES - 2)>();
             __builtin_amdgcn_sched_barrier(0);
             read_frags(T::KK & 1, smem + nxt * T::STAGE_BYTES, 0);
-            issue_loads(cur, ks + T::STAGES);
+            if constexpr (LD) issue_load_range(cur, ks + T::STAGES, 0, T::LATE);
             mma((T::KK - 1) & 1);
             __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
 #pragma unroll
             for (int i = 0; i < T::FM * T::FN; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);          // one MFMA
-                if (i < T::LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // one load
+                constexpr int L = LD ? T::LATE : 0;
+                const int nl = L * (i + 1) / (T::FM * T::FN) - L * i / (T::FM * T::FN);
+                sched_vmem<1>(nl);                                              // loads
             }
             cur = nxt;
         }
+    };
+    if (nk > 0) {
+        if (T::LOADERS == T::WAVES || loader)
+            main_loop(Flag<true>{});
+        else
+            main_loop(Flag<false>{});
         // no global->LDS load may still be writing when the workgroup ends
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
@@ -503,8 +583,7 @@ gemm_nt_f16_stream(const _Float16* __restrict__ A, const _Float16* __restrict__ 
         issue_loads(s);
         advance_cursor();
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::LOADS * (T::STAGES - 2)));
-    __syncthreads();
+    lds_barrier<T::LOADS * (T::STAGES - 2)>();
     issue_loads(T::STAGES - 1);
     advance_cursor();
     read_frags(0, smem, 0);
@@ -530,10 +609,9 @@ gemm_nt_f16_stream(const _Float16* __restrict__ A, const _Float16* __restrict__ 
             // after it may be outstanding; after an epilogue its stores are
             // outstanding too, so wait for everything there).
             if (T::STAGES == 2 || ks == 0)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                lds_barrier<0>();
             else
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::LOADS * (T::STAGES - 2)));
-            __syncthreads();
+                lds_barrier<T::LOADS * (T::STAGES - 2)>();
             __builtin_amdgcn_sched_barrier(0);
             read_frags(T::KK & 1, smem + nxt * T::STAGE_BYTES, 0);
             issue_loads(cur);
@@ -1057,6 +1135,17 @@ gemm_nt_f16_simple(const _Float16* __restrict__ A, const _Float16* __restrict__ 
 typedef TileShape<256, 256, 64, 2, 2, 2, 1> T256_k64_s2_w4;
 typedef TileShape<256, 256, 32, 2, 2, 4, 1> T256_k32_s4_w4;
 typedef TileShape<256, 256, 64, 2, 4, 2, 2> T256_k64_s2_w8;
+typedef TileShape<256, 256, 32, 2, 4, 4, 2> T256_k32_s4_w8;
+typedef TileShape<256, 256, 32, 2, 4, 5, 2> T256_k32_s5_w8;
+typedef TileShape<256, 256, 32, 2, 2, 5, 1> T256_k32_s5_w4;
+typedef TileShape<256, 256, 32, 2, 4, 4, 2, 2> T256_k32_s4_w8_e2;
+typedef TileShape<256, 256, 32, 2, 4, 5, 2, 2> T256_k32_s5_w8_e2;
+typedef TileShape<256, 256, 32, 2, 2, 4, 1, 4> T256_k32_s4_w4_e4;
+typedef TileShape<256, 256, 32, 2, 2, 5, 1, 4> T256_k32_s5_w4_e4;
+typedef TileShape<256, 256, 32, 2, 2, 5, 1, 8> T256_k32_s5_w4_e8;
+typedef TileShape<256, 256, 64, 2, 4, 2, 2, 0, 4> T256_k64_s2_w8_l4;
+typedef TileShape<256, 256, 32, 2, 4, 4, 2, 4, 4> T256_k32_s4_w8_e4_l4;
+typedef TileShape<256, 256, 32, 2, 4, 5, 2, 4, 4> T256_k32_s5_w8_e4_l4;
 typedef TileShape<256, 128, 64, 2, 2, 3, 1> T256x128_k64_s3_w4;
 typedef TileShape<128, 128, 64, 2, 2, 3, 1> T128_k64_s3_w4;
 typedef TileShape<64, 64, 64, 2, 2, 3, 2> T64_k64_s3_w4;
@@ -1164,10 +1253,21 @@ int launch_simple(const void* A, const void* B, void* C, int64_t M, int64_t N, i
 // Variant 0 is the default for large problems; the others are kept for
 // smaller shapes and as the measured alternatives (tile shape, ring depth,
 // persistence, hand-scheduled issue order).
-const Variant kVariants[] = {
+constexpr Variant kVariants[] = {
     {"mfma32_256x256x64_w8_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8>},
     {"mfma32_256x256x64_w4_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w4>},
     {"mfma32_256x256x32_w4_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w4>},
+    {"mfma32_256x256x32_w8_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w8>},
+    {"mfma32_256x256x32_w8_s5", 256, 256, 8, launch_mfma<T256_k32_s5_w8>},
+    {"mfma32_256x256x32_w4_s5", 256, 256, 8, launch_mfma<T256_k32_s5_w4>},
+    {"mfma32_256x256x32_w8_s4_e2", 256, 256, 8, launch_mfma<T256_k32_s4_w8_e2>},
+    {"mfma32_256x256x32_w8_s5_e2", 256, 256, 8, launch_mfma<T256_k32_s5_w8_e2>},
+    {"mfma32_256x256x32_w4_s4_e4", 256, 256, 8, launch_mfma<T256_k32_s4_w4_e4>},
+    {"mfma32_256x256x32_w4_s5_e4", 256, 256, 8, launch_mfma<T256_k32_s5_w4_e4>},
+    {"mfma32_256x256x32_w4_s5_e8", 256, 256, 8, launch_mfma<T256_k32_s5_w4_e8>},
+    {"mfma32_256x256x64_w8_s2_l4", 256, 256, 8, launch_mfma<T256_k64_s2_w8_l4>},
+    {"mfma32_256x256x32_w8_s4_e4_l4", 256, 256, 8, launch_mfma<T256_k32_s4_w8_e4_l4>},
+    {"mfma32_256x256x32_w8_s5_e4_l4", 256, 256, 8, launch_mfma<T256_k32_s5_w8_e4_l4>},
     {"mfma32_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4>},
     {"mfma32_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4>},
     {"mfma32_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4>},
@@ -1206,6 +1306,23 @@ bool mfma_eligible(const void* A, const void* B, int64_t K)
     return K % 8 == 0 && K < kMaxK && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0);
 }
 
+constexpr bool same_name(const char* a, const char* b)
+{
+    return *a == *b && (*a == 0 || same_name(a + 1, b + 1));
+}
+
+constexpr int variant_index(const char* name)
+{
+    for (int i = 0; i < kNumVariants; ++i)
+        if (same_name(kVariants[i].name, name)) return i;
+    return -1;
+}
+
+constexpr int kLarge = variant_index("mfma32_256x256x64_w8_s2");
+constexpr int kMedium = variant_index("mfma32_128x128x64_w4_s3");
+constexpr int kSmall = variant_index("mfma32_64x64x64_w4_s3");
+static_assert(kLarge >= 0 && kMedium >= 0 && kSmall >= 0, "selected variants are in the table");
+
 // Shape -> variant.  Prefer the largest tile that still gives the chip (256
 // CUs) about one tile per CU; smaller tiles only when the large one would
 // leave most CUs idle.
@@ -1213,9 +1330,9 @@ int select_mfma(int64_t M, int64_t N)
 {
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    if (t256 >= 192) return 0;  // 8-wave 256 x 256
-    if (t128 >= 192) return 4;  // 128 x 128
-    return 5;                   // 64 x 64
+    if (t256 >= 192) return kLarge;
+    if (t128 >= 192) return kMedium;
+    return kSmall;
 }
 }  // namespace
 
