@@ -126,8 +126,12 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
 //             with half of the waves loading, each SIMD runs one wave that
 //             never waits on the vector memory queue and keeps the matrix
 //             core busy while its partner issues loads
+//   DIST      how many MFMA k sub-steps ahead the fragments are read from
+//             LDS (1 .. KK); with DIST = KK a whole step is read ahead, the
+//             barrier sits at the start of the step and the step's loads
+//             spread over all of its MFMAs
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_, int EARLY_ = 0,
-          int LOADERS_ = 0>
+          int LOADERS_ = 0, int DIST_ = 1>
 struct TileShape {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -155,7 +159,9 @@ struct TileShape {
     static constexpr int B_LOADS = B_BYTES / 1024 / LOADERS;
     static constexpr int LOADS = A_LOADS + B_LOADS;                // per loading wave per step
     static constexpr int EARLY = EARLY_, LATE = LOADS - EARLY_;
-    static constexpr int R1_MFMAS = (KK - 1) * FM * FN;           // MFMAs before the barrier
+    static constexpr int DIST = DIST_;
+    static constexpr int R1_MFMAS = (KK - DIST) * FM * FN;        // MFMAs before the barrier
+    static constexpr int R2_MFMAS = DIST * FM * FN;               // MFMAs after it
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(ROWS_PER_LINE * CHUNKS == 16, "swizzle covers 16 lanes");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
@@ -166,7 +172,11 @@ struct TileShape {
     static_assert(STAGES >= 2 && LOADS * (STAGES - 2) <= 63, "vmcnt holds at most 63");
     static_assert(EARLY >= 0 && EARLY <= LOADS && (EARLY == 0 || STAGES >= 3),
                   "early loads need a free stage one step ahead");
-    static_assert(EARLY <= 4 * R1_MFMAS && LATE <= 4 * FM * FN, "at most 4 loads per MFMA");
+    static_assert(DIST >= 1 && DIST <= KK, "fragments are read 1 .. KK sub-steps ahead");
+    static_assert(EARLY == 0 || DIST < KK, "early loads go before the barrier");
+    static_assert((DIST == KK || (EARLY + KK - DIST - 1) / (KK - DIST) <= 4 * FM * FN) &&
+                      (LATE + DIST - 1) / DIST <= 4 * FM * FN,
+                  "at most 4 loads per MFMA");
 };
 
 // Scheduling group of n (0 .. 4, known after unrolling) vector memory
@@ -183,6 +193,11 @@ __device__ __forceinline__ void sched_vmem(int n)
 template <bool B>
 struct Flag {
     static constexpr bool value = B;
+};
+
+template <int V>
+struct Int {
+    static constexpr int value = V;
 };
 
 template <class T>
@@ -319,7 +334,13 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, 2 * kk + fr_hi) * 16;
 
-    half8_t fa[2][T::FM], fb[2][T::FN];
+    // Fragment registers.  With DIST = 1 two sets alternate by sub-step
+    // (KK is even, so sub-step kk always uses set kk % 2).  Otherwise set
+    // [p][kk] holds sub-step kk of a step with parity p; only the DIST + 1
+    // sets in flight are live at a time, and only those get registers.
+    constexpr int NSETS = T::DIST == 1 ? 2 : 2 * T::KK;
+    half8_t fa[NSETS][T::FM], fb[NSETS][T::FN];
+    auto set_of = [](int p, int kk) { return T::DIST == 1 ? (kk & 1) : p * T::KK + kk; };
     float16_t acc[T::FM][T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
@@ -328,22 +349,22 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto read_frags = [&](int buf, const unsigned char* stage_base, int kk) {
+    auto read_frags = [&](int p, const unsigned char* stage_base, int kk) {
         const unsigned char* pa = stage_base + a_row0 * T::ROW_BYTES + fr_pos[kk];
         const unsigned char* pb = stage_base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[kk];
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i) fa[buf][i] = *(const half8_t*)(pa + i * 32 * T::ROW_BYTES);
+        for (int i = 0; i < T::FM; ++i) fa[set_of(p, kk)][i] = *(const half8_t*)(pa + i * 32 * T::ROW_BYTES);
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) fb[buf][j] = *(const half8_t*)(pb + j * 32 * T::ROW_BYTES);
+        for (int j = 0; j < T::FN; ++j) fb[set_of(p, kk)][j] = *(const half8_t*)(pb + j * 32 * T::ROW_BYTES);
     };
 
-    auto mma = [&](int buf) {
+    auto mma = [&](int p, int kk) {
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
             for (int j = 0; j < T::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[buf][j], fa[buf][i], acc[i][j],
-                                                                   0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[set_of(p, kk)][j], fa[set_of(p, kk)][i],
+                                                                   acc[i][j], 0, 0, 0);
     };
 
     const int nk = (K + T::BK - 1) / T::BK;
@@ -352,29 +373,32 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     // issued STAGES - 1 steps earlier.  Before step ks + 1 is read, each wave
     // waits until its own loads of that step have landed (vmcnt: only the
     // loads of the STAGES - 2 later steps may still be outstanding) and a
-    // barrier makes all waves' loads visible; the same barrier (its fence
-    // drains this wave's LDS reads) also guarantees every wave has finished
-    // reading step ks's stage, which is then refilled with step ks + STAGES.
+    // barrier makes all waves' loads visible; since every wave has also
+    // finished its LDS reads of step ks by then (lgkmcnt(0) before the
+    // barrier), step ks's stage is free after it and is refilled with step
+    // ks + STAGES.
     //
-    // Issue order inside a step (pinned with scheduling-group barriers, so
-    // the matrix core always has independent work queued):
-    //   sub-steps 0 .. KK-2:  fragment reads of sub-step kk+1, then the
-    //                         FM*FN MFMAs of sub-step kk;
-    //   after the barrier:    fragment reads of the next step's sub-step 0,
-    //                         then the MFMAs of sub-step KK-1, each followed
-    //                         by one of the wave's global->LDS loads.
+    // Fragments of sub-step kk are read DIST sub-steps before its MFMAs, so
+    // a step splits at the barrier (pinned with scheduling-group barriers,
+    // so the matrix core always has independent work queued):
+    //   before:  sub-steps 0 .. KK-DIST-1: fragment reads of sub-step
+    //            kk+DIST, then the FM*FN MFMAs of sub-step kk;
+    //   after:   sub-steps KK-DIST .. KK-1: fragment reads of the next
+    //            step's sub-step kk+DIST-KK, then the MFMAs of sub-step kk,
+    //            with the step's loads spread between them.
     //
     // With EARLY > 0 a step's loads go out in two parts: the first LATE right
     // after the barrier that frees their stage, the last EARLY during the
-    // next step's MFMAs before its barrier, one every R1_MFMAS / EARLY MFMAs.
-    // Spreading them keeps the vector memory unit's queue short, so a load
-    // waiting for a queue slot does not hold up the MFMAs behind it.  Loads
-    // leave in the same order either way, so the vmcnt count at each barrier
-    // is unchanged: only the STAGES - 2 steps after the next one may be in
-    // flight.
+    // next step's MFMAs before its barrier.  Spreading them keeps the vector
+    // memory queue short, so a load waiting for a queue slot does not hold up
+    // the MFMAs behind it.  Loads leave in the same order either way, so the
+    // vmcnt count at each barrier is unchanged: only the STAGES - 2 steps
+    // after the next one may be in flight.
+    //
     // The loop is compiled twice: for loading waves and, when only some
     // waves load, for the others (no loads, and nothing in flight at the
-    // barriers).
+    // barriers).  With DIST > 1 its body covers two steps, so the fragment
+    // set parity is known at compile time.
     auto main_loop = [&](auto tag) {
         constexpr bool LD = decltype(tag)::value;
 #pragma unroll
@@ -382,46 +406,64 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
             if constexpr (LD) issue_loads(s, s);
         lds_barrier<T::LOADS * (T::STAGES - 2)>();
         if constexpr (LD) issue_load_range(T::STAGES - 1, T::STAGES - 1, 0, T::LATE);
-        read_frags(0, smem, 0);
+#pragma unroll
+        for (int kk = 0; kk < T::DIST; ++kk) read_frags(0, smem, kk);
 
         int cur = 0;  // stage of step ks
-        for (int ks = 0; ks < nk; ++ks) {
+        auto step = [&](int ks, auto parity) {
+            constexpr int P = decltype(parity)::value;
+            constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
             const unsigned char* base = smem + cur * T::STAGE_BYTES;
             const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
             const int prv = cur == 0 ? T::STAGES - 1 : cur - 1;  // free since the last barrier
+            // Each sub-step is its own scheduling region (fenced with
+            // sched_barrier), so MFMAs of different sub-steps never
+            // interleave into back-to-back dependent pairs.
 #pragma unroll
-            for (int kk = 0; kk + 1 < T::KK; ++kk) {
-                read_frags((kk + 1) & 1, base, kk + 1);
-                mma(kk & 1);
-            }
-            if constexpr (LD && T::EARLY > 0) issue_load_range(prv, ks + T::STAGES - 1, T::LATE, T::EARLY);
-#pragma unroll
-            for (int kk = 0; kk + 1 < T::KK; ++kk) {
+            for (int kk = 0; kk < T::KK - T::DIST; ++kk) {
+                constexpr int E = LD ? T::EARLY : 0;
+                constexpr int R1 = T::KK - T::DIST > 0 ? T::KK - T::DIST : 1;
+                const int e0 = E * kk / R1, e1 = E * (kk + 1) / R1;  // this sub-step's early loads
+                read_frags(P, base, kk + T::DIST);
+                mma(P, kk);
+                if constexpr (E > 0) issue_load_range(prv, ks + T::STAGES - 1, T::LATE + e0, e1 - e0);
                 __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
 #pragma unroll
-                for (int i = 0; i < T::FM * T::FN; ++i) {
+                for (int i = 0; i < G; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-                    constexpr int E = LD ? T::EARLY : 0;
-                    const int n = kk * T::FM * T::FN + i;
-                    const int nl = E * (n + 1) / T::R1_MFMAS - E * n / T::R1_MFMAS;
-                    sched_vmem<0>(nl);                                          // loads
+                    sched_vmem<0>((e1 - e0) * (i + 1) / G - (e1 - e0) * i / G);  // loads
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
             lds_barrier<T::LOADS * (T::STAGES - 2)>();
             __builtin_amdgcn_sched_barrier(0);
-            read_frags(T::KK & 1, smem + nxt * T::STAGE_BYTES, 0);
-            if constexpr (LD) issue_load_range(cur, ks + T::STAGES, 0, T::LATE);
-            mma((T::KK - 1) & 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
+            const unsigned char* next = smem + nxt * T::STAGE_BYTES;
 #pragma unroll
-            for (int i = 0; i < T::FM * T::FN; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);          // one MFMA
+            for (int d = 0; d < T::DIST; ++d) {
                 constexpr int L = LD ? T::LATE : 0;
-                const int nl = L * (i + 1) / (T::FM * T::FN) - L * i / (T::FM * T::FN);
-                sched_vmem<1>(nl);                                              // loads
+                const int l0 = L * d / T::DIST, l1 = L * (d + 1) / T::DIST;  // this sub-step's loads
+                read_frags(1 - P, next, d);
+                mma(P, T::KK - T::DIST + d);
+                if constexpr (L > 0) issue_load_range(cur, ks + T::STAGES, l0, l1 - l0);
+                __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);          // one MFMA
+                    sched_vmem<1>((l1 - l0) * (i + 1) / G - (l1 - l0) * i / G);  // loads
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             cur = nxt;
+        };
+        if constexpr (T::DIST == 1) {
+            for (int ks = 0; ks < nk; ++ks) step(ks, Int<0>{});
+        } else {
+            int ks = 0;
+            for (; ks + 1 < nk; ks += 2) {
+                step(ks, Int<0>{});
+                step(ks + 1, Int<1>{});
+            }
+            if (ks < nk) step(ks, Int<0>{});
         }
     };
     if (nk > 0) {
@@ -1131,21 +1173,13 @@ gemm_nt_f16_simple(const _Float16* __restrict__ A, const _Float16* __restrict__ 
 
 // ------------------------------------------------------------------ host --
 
-//                  BM   BN   BK  WM  WN  S  OCC
-typedef TileShape<256, 256, 64, 2, 2, 2, 1> T256_k64_s2_w4;
-typedef TileShape<256, 256, 32, 2, 2, 4, 1> T256_k32_s4_w4;
+//                  BM   BN   BK  WM  WN  S  OCC EARLY LOADERS DIST
 typedef TileShape<256, 256, 64, 2, 4, 2, 2> T256_k64_s2_w8;
-typedef TileShape<256, 256, 32, 2, 4, 4, 2> T256_k32_s4_w8;
+typedef TileShape<256, 256, 64, 2, 2, 2, 1> T256_k64_s2_w4;
 typedef TileShape<256, 256, 32, 2, 4, 5, 2> T256_k32_s5_w8;
-typedef TileShape<256, 256, 32, 2, 2, 5, 1> T256_k32_s5_w4;
-typedef TileShape<256, 256, 32, 2, 4, 4, 2, 2> T256_k32_s4_w8_e2;
-typedef TileShape<256, 256, 32, 2, 4, 5, 2, 2> T256_k32_s5_w8_e2;
-typedef TileShape<256, 256, 32, 2, 2, 4, 1, 4> T256_k32_s4_w4_e4;
-typedef TileShape<256, 256, 32, 2, 2, 5, 1, 4> T256_k32_s5_w4_e4;
-typedef TileShape<256, 256, 32, 2, 2, 5, 1, 8> T256_k32_s5_w4_e8;
+typedef TileShape<256, 256, 32, 2, 4, 4, 2, 0, 0, 2> T256_k32_s4_w8_d2;
 typedef TileShape<256, 256, 64, 2, 4, 2, 2, 0, 4> T256_k64_s2_w8_l4;
-typedef TileShape<256, 256, 32, 2, 4, 4, 2, 4, 4> T256_k32_s4_w8_e4_l4;
-typedef TileShape<256, 256, 32, 2, 4, 5, 2, 4, 4> T256_k32_s5_w8_e4_l4;
+typedef TileShape<256, 256, 32, 2, 2, 5, 1, 4> T256_k32_s5_w4_e4;
 typedef TileShape<256, 128, 64, 2, 2, 3, 1> T256x128_k64_s3_w4;
 typedef TileShape<128, 128, 64, 2, 2, 3, 1> T128_k64_s3_w4;
 typedef TileShape<64, 64, 64, 2, 2, 3, 2> T64_k64_s3_w4;
@@ -1256,18 +1290,10 @@ int launch_simple(const void* A, const void* B, void* C, int64_t M, int64_t N, i
 constexpr Variant kVariants[] = {
     {"mfma32_256x256x64_w8_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8>},
     {"mfma32_256x256x64_w4_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w4>},
-    {"mfma32_256x256x32_w4_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w4>},
-    {"mfma32_256x256x32_w8_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w8>},
     {"mfma32_256x256x32_w8_s5", 256, 256, 8, launch_mfma<T256_k32_s5_w8>},
-    {"mfma32_256x256x32_w4_s5", 256, 256, 8, launch_mfma<T256_k32_s5_w4>},
-    {"mfma32_256x256x32_w8_s4_e2", 256, 256, 8, launch_mfma<T256_k32_s4_w8_e2>},
-    {"mfma32_256x256x32_w8_s5_e2", 256, 256, 8, launch_mfma<T256_k32_s5_w8_e2>},
-    {"mfma32_256x256x32_w4_s4_e4", 256, 256, 8, launch_mfma<T256_k32_s4_w4_e4>},
-    {"mfma32_256x256x32_w4_s5_e4", 256, 256, 8, launch_mfma<T256_k32_s5_w4_e4>},
-    {"mfma32_256x256x32_w4_s5_e8", 256, 256, 8, launch_mfma<T256_k32_s5_w4_e8>},
+    {"mfma32_256x256x32_w8_s4_d2", 256, 256, 8, launch_mfma<T256_k32_s4_w8_d2>},
     {"mfma32_256x256x64_w8_s2_l4", 256, 256, 8, launch_mfma<T256_k64_s2_w8_l4>},
-    {"mfma32_256x256x32_w8_s4_e4_l4", 256, 256, 8, launch_mfma<T256_k32_s4_w8_e4_l4>},
-    {"mfma32_256x256x32_w8_s5_e4_l4", 256, 256, 8, launch_mfma<T256_k32_s5_w8_e4_l4>},
+    {"mfma32_256x256x32_w4_s5_e4", 256, 256, 8, launch_mfma<T256_k32_s5_w4_e4>},
     {"mfma32_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4>},
     {"mfma32_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4>},
     {"mfma32_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4>},
