@@ -242,9 +242,63 @@ __device__ __forceinline__ void epilogue(const float16_t (&acc)[T::FM][T::FN], _
     }
 }
 
+// Epilogue through LDS, for C rows that take aligned 16-byte stores (N % 8
+// == 0, C 16-byte aligned).  The ring is dead once the K loop has ended, and
+// the whole BM x BN fp16 tile fits in it.  Each wave writes its accumulators
+// (fp32 -> fp16, round to nearest even) into a row-major copy of the tile,
+// then every wave reads back whole rows, 16 bytes per lane, and stores them:
+// each store instruction covers complete rows of the tile, so C is written
+// in full cache lines instead of the scattered 8-byte pieces each lane holds.
+// In LDS, 16-byte chunk c of row r sits at position c ^ (r % SW), so the
+// 8-byte writes of 32 rows at one column touch 16 bank groups (2-way at
+// most) and the 16-byte row reads are conflict-free.
+template <class T>
+__device__ __forceinline__ void epilogue_lds(const float16_t (&acc)[T::FM][T::FN], _Float16* __restrict__ C,
+                                             int M, int N, int m0, int n0, int wm, int wn, int lane, int wave,
+                                             unsigned char* smem)
+{
+    constexpr int PITCH = T::BN * 2;              // bytes per tile row
+    constexpr int CH = T::BN / 8;                  // 16-byte chunks per row
+    constexpr int SW = CH >= 16 ? 15 : CH - 1;
+    constexpr int RPL = 1024 / PITCH;              // rows per wave-wide 1 KiB read
+    constexpr int ITERS = T::BM / RPL / T::WAVES;  // reads per wave
+    static_assert(T::BM * PITCH <= T::LDS_BYTES, "the C tile fits in the ring");
+    static_assert(RPL >= 1 && ITERS * RPL * T::WAVES == T::BM, "rows split evenly over waves");
+    const int fr_row = lane & 31, fr_hi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+        const int r = wm * T::WTM + i * 32 + fr_row;
+        unsigned char* lrow = smem + r * PITCH;
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = wn * T::WTN + j * 32 + 8 * q + 4 * fr_hi;
+                half4_t h;
+                h[0] = (_Float16)acc[i][j][4 * q + 0];
+                h[1] = (_Float16)acc[i][j][4 * q + 1];
+                h[2] = (_Float16)acc[i][j][4 * q + 2];
+                h[3] = (_Float16)acc[i][j][4 * q + 3];
+                *(half4_t*)(lrow + (((col >> 3) ^ (r & SW)) << 4) + (col & 4) * 2) = h;
+            }
+        }
+    }
+    __syncthreads();
+    const int lr = lane / CH, lc = lane % CH;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int r = (wave * ITERS + it) * RPL + lr;
+        const half8_t v = *(const half8_t*)(smem + r * PITCH + ((lc ^ (r & SW)) << 4));
+        const int m = m0 + r, n = n0 + lc * 8;
+        if (m < M && n < N) *(half8_t*)(C + (size_t)m * N + n) = v;
+    }
+}
+
 // Main MFMA kernel.  Requirements checked on the host: A and B 16-byte
-// aligned, K % 8 == 0, K < 2^22, M, N < 2^31.  `c_vec` says whether C rows
-// allow aligned 8-byte stores (N % 4 == 0 and C 8-byte aligned).
+// aligned, K % 8 == 0, K < 2^22, M, N < 2^31.  `c_vec` says which stores C
+// rows allow: 2 for aligned 16-byte stores (N % 8 == 0, C 16-byte aligned;
+// the tile then leaves through LDS), 1 for aligned 8-byte stores (N % 4 ==
+// 0, C 8-byte aligned), 0 for single elements.
 template <class T>
 __global__ void __launch_bounds__(T::THREADS, T::OCC)
 gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
@@ -472,10 +526,18 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
         else
             main_loop(Flag<false>{});
         // no global->LDS load may still be writing when the workgroup ends
+        // (nor when the ring is reused for the epilogue below)
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
 
-    epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
+    // Small tiles (64 x 64) keep the direct stores: their epilogue is short
+    // and the two extra barriers cost more than the wider stores save.
+    if (T::BM * T::BN >= 128 * 128 && c_vec == 2) {
+        __syncthreads();  // every wave is done with the ring
+        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem);
+    } else {
+        epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
+    }
 }
 
 // Persistent streaming variant of the kernel above.  The grid holds one
@@ -1200,7 +1262,7 @@ int launch_mfma(const void* A, const void* B, void* C, int64_t M, int64_t N, int
 {
     const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
-    const int c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
+    const int c_vec = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 2 : ((N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0);
     hipLaunchKernelGGL((gemm_nt_f16_mfma<T>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS),
                        0, stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M,
                        (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
@@ -1344,21 +1406,48 @@ constexpr int variant_index(const char* name)
     return -1;
 }
 
-constexpr int kLarge = variant_index("mfma32_256x256x64_w8_s2");
-constexpr int kMedium = variant_index("mfma32_128x128x64_w4_s3");
-constexpr int kSmall = variant_index("mfma32_64x64x64_w4_s3");
-static_assert(kLarge >= 0 && kMedium >= 0 && kSmall >= 0, "selected variants are in the table");
+// Shape -> variant.  Four tile sizes compete; each is priced as
+//   ceil(tiles / 256 CUs) x (tile flops / per-CU rate + fixed cost),
+// i.e. whole waves of tiles over the chip (one workgroup per CU), with the
+// per-CU rate each kernel sustains on a full chip (measured on MI355X at
+// 4096^3 .. 8192^3, fp16 random data) and a fixed per-wave cost for launch,
+// pipeline fill and epilogue.  Small problems then take small tiles (more
+// CUs busy), large ones the 256 x 256 kernel (most reuse per byte loaded).
+struct Candidate {
+    int variant;
+    int bm, bn;
+    double tflops_chip;  // sustained on a full chip
+};
 
-// Shape -> variant.  Prefer the largest tile that still gives the chip (256
-// CUs) about one tile per CU; smaller tiles only when the large one would
-// leave most CUs idle.
-int select_mfma(int64_t M, int64_t N)
+constexpr int kCUs = 256;
+constexpr double kWaveCostUs = 3.0;
+constexpr Candidate kCandidates[] = {
+    {variant_index("mfma32_256x256x64_w8_s2"), 256, 256, 1100.0},
+    {variant_index("mfma32_256x128x64_w4_s3"), 256, 128, 1000.0},
+    {variant_index("mfma32_128x128x64_w4_s3"), 128, 128, 900.0},
+    {variant_index("mfma32_64x64x64_w4_s3"), 64, 64, 650.0},
+};
+static_assert(variant_index("mfma32_256x256x64_w8_s2") >= 0 && variant_index("mfma32_256x128x64_w4_s3") >= 0 &&
+                  variant_index("mfma32_128x128x64_w4_s3") >= 0 && variant_index("mfma32_64x64x64_w4_s3") >= 0,
+              "selected variants are in the table");
+
+int select_mfma(int64_t M, int64_t N, int64_t K)
 {
-    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    if (t256 >= 192) return kLarge;
-    if (t128 >= 192) return kMedium;
-    return kSmall;
+    int best = kCandidates[0].variant;
+    double best_us = 0;
+    bool first = true;
+    for (const Candidate& c : kCandidates) {
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        const int64_t waves = (tiles + kCUs - 1) / kCUs;
+        const double tile_us = 2.0 * c.bm * c.bn * (double)K / (c.tflops_chip * 1e12 / kCUs) * 1e6;
+        const double us = (double)waves * (tile_us + kWaveCostUs);
+        if (first || us < best_us) {
+            best = c.variant;
+            best_us = us;
+            first = false;
+        }
+    }
+    return best;
 }
 }  // namespace
 
@@ -1378,7 +1467,7 @@ int32_t gemm_nt_f16_select(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N < 0 || K < 0 || M > kMaxMN || N > kMaxMN || K > kMaxMN) return -1;
     if (K % 8 != 0 || K >= kMaxK) return kSimple;
-    return select_mfma(M, N);
+    return select_mfma(M, N, K);
 }
 
 const char* gemm_nt_f16_config_name(int64_t M, int64_t N, int64_t K)
@@ -1395,7 +1484,7 @@ int gemm_nt_f16_ex(const void* A, const void* B, void* C, int64_t M, int64_t N, 
     if (variant >= kNumVariants) return hipErrorInvalidValue;
     if (M == 0 || N == 0) return hipSuccess;
     const bool fast = mfma_eligible(A, B, K);
-    if (variant < 0) variant = fast ? select_mfma(M, N) : kSimple;
+    if (variant < 0) variant = fast ? select_mfma(M, N, K) : kSimple;
     else if (variant != kSimple && !fast) return hipErrorInvalidValue;
     const Variant& v = kVariants[variant];
     return v.launch(A, B, C, M, N, K, v.group_m, stream);

@@ -331,6 +331,30 @@ def test_no_writes_outside_c():
                               c16.view(np.uint16)), name
 
 
+@pytest.mark.parametrize("N,offset", [(264, 0), (264, 4), (264, 1), (260, 0), (262, 0)])
+def test_every_store_path_every_variant(N, offset):
+    """C rows taking 16-byte stores (through LDS), 8-byte stores, or single
+    elements, chosen by N and by C's alignment (offset in elements from a
+    16-byte boundary); guard bands on both sides must stay untouched."""
+    torch = _torch()
+    M, K = 300, 136
+    a, b = workloads.small_integers(M, N, K, seed=N * 31 + offset)
+    _, c16 = oracle.gemm_nt(a, b)
+    guard = 4096
+    ta = torch.from_numpy(a).to(dev())
+    tb = torch.from_numpy(b).to(dev())
+    for name, vid in variant_ids().items():
+        print("case stores", N, offset, name, flush=True)
+        buf = torch.full((guard + offset + M * N + guard,), -3.0, dtype=torch.float16, device=dev())
+        out = buf[guard + offset:guard + offset + M * N].view(M, N)
+        binding.gemm_nt_f16_ex(ta, tb, out=out, variant=vid)
+        torch.cuda.synchronize()
+        host = buf.cpu().numpy()
+        assert np.all(host[:guard + offset] == -3.0) and np.all(host[-guard:] == -3.0), name
+        assert np.array_equal(host[guard + offset:-guard].reshape(M, N).view(np.uint16),
+                              c16.view(np.uint16)), name
+
+
 def test_repeated_launches_are_deterministic_and_finite():
     torch = _torch()
     _, a, b = workload_data("square_4096")
