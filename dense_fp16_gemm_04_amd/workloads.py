@@ -39,15 +39,20 @@ class Workload:
         return 2 * self.M * self.N * self.K
 
 
-# The five problem sizes: three square throughput points, the 8192 cube
-# (headline throughput and the long-K error point) and a ragged shape whose
-# sizes are multiples of no tile size (partial tiles in M, N and K).
+# The problem sizes: three square throughput points, the 8192 cube (headline
+# throughput and the long-K error point), a ragged shape whose sizes are
+# multiples of no tile size (partial tiles in M, N and K), and the two
+# one-GPU shares of the cube.
 WORKLOADS = (
     Workload("square_256", 256, 256, 256, 0),
     Workload("square_1024", 1024, 1024, 1024, 1),
     Workload("square_4096", 4096, 4096, 4096, 2),
     Workload("square_8192", 8192, 8192, 8192, 3),
     Workload("ragged_5000x3000x6000", 5000, 3000, 6000, 4),
+    # one GPU's share of the 8192 cube split eight ways along M (A's rows) or
+    # along N (B's rows): what a single GPU runs when the product is sharded
+    Workload("share_m_1024x8192x8192", 1024, 8192, 8192, 5),
+    Workload("share_n_8192x1024x8192", 8192, 1024, 8192, 6),
 )
 
 HEADLINE = WORKLOADS[3]

@@ -97,7 +97,8 @@ def workload_oracle(name):
     return oracle.gemm_nt(a, b)
 
 
-FULL = ["square_256", "square_1024", "square_4096", "ragged_5000x3000x6000"]
+FULL = ["square_256", "square_1024", "square_4096", "ragged_5000x3000x6000",
+        "share_m_1024x8192x8192", "share_n_8192x1024x8192"]
 
 
 @pytest.mark.parametrize("name", FULL)
