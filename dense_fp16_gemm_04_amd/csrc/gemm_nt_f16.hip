@@ -57,6 +57,20 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Accumulator block of one lane: 16 floats for a 32x32 MFMA block, 4 for a
+// 16x16 one.
+template <int MI>
+struct AccBlock;
+template <>
+struct AccBlock<32> {
+    using type = float16_t;
+};
+template <>
+struct AccBlock<16> {
+    using type = float4_t;
+};
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -130,15 +144,24 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
 //             LDS (1 .. KK); with DIST = KK a whole step is read ahead, the
 //             barrier sits at the start of the step and the step's loads
 //             spread over all of its MFMAs
+//   MI        MFMA block: 32 (v_mfma_f32_32x32x16_f16) or 16
+//             (v_mfma_f32_16x16x32_f16: half the work per instruction, the
+//             same bytes of operands per flop from LDS)
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_, int EARLY_ = 0,
-          int LOADERS_ = 0, int DIST_ = 1>
+          int LOADERS_ = 0, int DIST_ = 1, int MI_ = 32>
 struct TileShape {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M * WAVES_N, THREADS = WAVES * kWave;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave sub-tile
-    static constexpr int FM = WTM / 32, FN = WTN / 32;            // 32x32 blocks per wave
-    static constexpr int KK = BK / 16;                             // MFMA k sub-steps per step
+    static constexpr int MI = MI_;                                 // MFMA block edge
+    static constexpr int KPI = MI == 32 ? 16 : 32;                 // k per MFMA
+    static constexpr int CPS = KPI / 8;                            // 16-byte k chunks per MFMA
+    static constexpr int ACC = MI * MI / kWave;                    // accumulator floats per lane per block
+    static constexpr int NG = ACC / 4;                             // groups of 4 consecutive columns
+    using acc_t = typename AccBlock<MI>::type;
+    static constexpr int FM = WTM / MI, FN = WTN / MI;            // MFMA blocks per wave
+    static constexpr int KK = BK / KPI;                            // MFMA k sub-steps per step
     static constexpr int STAGES = STAGES_;
     static constexpr int OCC = OCC_;
     static constexpr int ROW_BYTES = BK * 2;
@@ -164,7 +187,8 @@ struct TileShape {
     static constexpr int R2_MFMAS = DIST * FM * FN;               // MFMAs after it
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(ROWS_PER_LINE * CHUNKS == 16, "swizzle covers 16 lanes");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(MI == 32 || MI == 16, "MFMA block is 32x32 or 16x16");
+    static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be whole MFMA blocks");
     static_assert(LOADERS >= 1 && LOADERS <= WAVES, "loading waves are a subset of the waves");
     static_assert(A_LOADS * LOADERS * 1024 == A_BYTES, "A tile must split evenly over loading waves");
     static_assert(B_LOADS * LOADERS * 1024 == B_BYTES, "B tile must split evenly over loading waves");
@@ -206,25 +230,25 @@ __device__ __forceinline__ int swz(int row, int chunk)
     return chunk ^ ((row >> T::SWZ_SHIFT) & (T::CHUNKS - 1));
 }
 
-// Epilogue: fp32 -> fp16 (round to nearest even) and store.  In each 32x32
-// block lane l holds row cm (= its row of the first block) and, in
-// accumulator registers 4q .. 4q+3, the four consecutive columns
-// cn + 8q .. cn + 8q + 3, written with one 8-byte store.  Rows past M and
-// columns past N are not written.
+// Epilogue: fp32 -> fp16 (round to nearest even) and store.  In each MFMA
+// block lane l holds row cm (its row in the first block) and, in accumulator
+// registers 4q .. 4q+3, the four consecutive columns cn + 8q .. cn + 8q + 3,
+// written with one 8-byte store.  Rows past M and columns past N are not
+// written.
 template <class T>
-__device__ __forceinline__ void epilogue(const float16_t (&acc)[T::FM][T::FN], _Float16* __restrict__ C,
+__device__ __forceinline__ void epilogue(const typename T::acc_t (&acc)[T::FM][T::FN], _Float16* __restrict__ C,
                                          int M, int N, int cm, int cn, int c_vec)
 {
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
-        const int m = cm + i * 32;
+        const int m = cm + i * T::MI;
         if (m >= M) continue;
         _Float16* crow = C + (size_t)m * N;
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = cn + j * 32 + 8 * q;
+            for (int q = 0; q < T::NG; ++q) {
+                const int n = cn + j * T::MI + 8 * q;
                 half4_t h;
                 h[0] = (_Float16)acc[i][j][4 * q + 0];
                 h[1] = (_Float16)acc[i][j][4 * q + 1];
@@ -253,7 +277,7 @@ __device__ __forceinline__ void epilogue(const float16_t (&acc)[T::FM][T::FN], _
 // 8-byte writes of 32 rows at one column touch 16 bank groups (2-way at
 // most) and the 16-byte row reads are conflict-free.
 template <class T>
-__device__ __forceinline__ void epilogue_lds(const float16_t (&acc)[T::FM][T::FN], _Float16* __restrict__ C,
+__device__ __forceinline__ void epilogue_lds(const typename T::acc_t (&acc)[T::FM][T::FN], _Float16* __restrict__ C,
                                              int M, int N, int m0, int n0, int wm, int wn, int lane, int wave,
                                              unsigned char* smem)
 {
@@ -264,16 +288,16 @@ __device__ __forceinline__ void epilogue_lds(const float16_t (&acc)[T::FM][T::FN
     constexpr int ITERS = T::BM / RPL / T::WAVES;  // reads per wave
     static_assert(T::BM * PITCH <= T::LDS_BYTES, "the C tile fits in the ring");
     static_assert(RPL >= 1 && ITERS * RPL * T::WAVES == T::BM, "rows split evenly over waves");
-    const int fr_row = lane & 31, fr_hi = lane >> 5;
+    const int fr_row = lane % T::MI, fr_hi = lane / T::MI;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
-        const int r = wm * T::WTM + i * 32 + fr_row;
+        const int r = wm * T::WTM + i * T::MI + fr_row;
         unsigned char* lrow = smem + r * PITCH;
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = wn * T::WTN + j * 32 + 8 * q + 4 * fr_hi;
+            for (int q = 0; q < T::NG; ++q) {
+                const int col = wn * T::WTN + j * T::MI + 8 * q + 4 * fr_hi;
                 half4_t h;
                 h[0] = (_Float16)acc[i][j][4 * q + 0];
                 h[1] = (_Float16)acc[i][j][4 * q + 1];
@@ -380,36 +404,37 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     // 2 * kk + l / 32 for k sub-step kk (16 k values per MFMA).  Row offsets
     // within a block are multiples of 32, so the swizzle term depends only on
     // l % 32 and is the same for every block.
-    const int fr_row = lane & 31;
-    const int fr_hi = lane >> 5;
+    const int fr_row = lane % T::MI;
+    const int fr_hi = lane / T::MI;
     const int a_row0 = wm * T::WTM + fr_row;
     const int b_row0 = wn * T::WTN + fr_row;
     int fr_pos[T::KK];
 #pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, 2 * kk + fr_hi) * 16;
+    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, T::CPS * kk + fr_hi) * 16;
 
-    // Fragment registers.  With DIST = 1 two sets alternate by sub-step
-    // (KK is even, so sub-step kk always uses set kk % 2).  Otherwise set
+    // Fragment registers.  With DIST = 1 and KK even two sets alternate by
+    // sub-step (sub-step kk always uses set kk % 2).  Otherwise set
     // [p][kk] holds sub-step kk of a step with parity p; only the DIST + 1
     // sets in flight are live at a time, and only those get registers.
-    constexpr int NSETS = T::DIST == 1 ? 2 : 2 * T::KK;
+    constexpr bool ALT = T::DIST == 1 && T::KK % 2 == 0;  // sets alternate by sub-step
+    constexpr int NSETS = ALT ? 2 : 2 * T::KK;
     half8_t fa[NSETS][T::FM], fb[NSETS][T::FN];
-    auto set_of = [](int p, int kk) { return T::DIST == 1 ? (kk & 1) : p * T::KK + kk; };
-    float16_t acc[T::FM][T::FN];
+    auto set_of = [](int p, int kk) { return ALT ? (kk & 1) : p * T::KK + kk; };
+    typename T::acc_t acc[T::FM][T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < T::ACC; ++r) acc[i][j][r] = 0.0f;
 
     auto read_frags = [&](int p, const unsigned char* stage_base, int kk) {
         const unsigned char* pa = stage_base + a_row0 * T::ROW_BYTES + fr_pos[kk];
         const unsigned char* pb = stage_base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[kk];
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i) fa[set_of(p, kk)][i] = *(const half8_t*)(pa + i * 32 * T::ROW_BYTES);
+        for (int i = 0; i < T::FM; ++i) fa[set_of(p, kk)][i] = *(const half8_t*)(pa + i * T::MI * T::ROW_BYTES);
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) fb[set_of(p, kk)][j] = *(const half8_t*)(pb + j * 32 * T::ROW_BYTES);
+        for (int j = 0; j < T::FN; ++j) fb[set_of(p, kk)][j] = *(const half8_t*)(pb + j * T::MI * T::ROW_BYTES);
     };
 
     auto mma = [&](int p, int kk) {
@@ -417,8 +442,12 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
             for (int j = 0; j < T::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[set_of(p, kk)][j], fa[set_of(p, kk)][i],
-                                                                   acc[i][j], 0, 0, 0);
+                if constexpr (T::MI == 32)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[set_of(p, kk)][j], fa[set_of(p, kk)][i],
+                                                                       acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[set_of(p, kk)][j], fa[set_of(p, kk)][i],
+                                                                       acc[i][j], 0, 0, 0);
     };
 
     const int nk = (K + T::BK - 1) / T::BK;
@@ -451,8 +480,8 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     //
     // The loop is compiled twice: for loading waves and, when only some
     // waves load, for the others (no loads, and nothing in flight at the
-    // barriers).  With DIST > 1 its body covers two steps, so the fragment
-    // set parity is known at compile time.
+    // barriers).  Unless the sets alternate by sub-step, its body covers two
+    // steps, so the fragment set parity is known at compile time.
     auto main_loop = [&](auto tag) {
         constexpr bool LD = decltype(tag)::value;
 #pragma unroll
@@ -509,7 +538,7 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
             }
             cur = nxt;
         };
-        if constexpr (T::DIST == 1) {
+        if constexpr (ALT) {
             for (int ks = 0; ks < nk; ++ks) step(ks, Int<0>{});
         } else {
             int ks = 0;
@@ -1242,6 +1271,16 @@ typedef TileShape<256, 256, 32, 2, 4, 5, 2> T256_k32_s5_w8;
 typedef TileShape<256, 256, 32, 2, 4, 4, 2, 0, 0, 2> T256_k32_s4_w8_d2;
 typedef TileShape<256, 256, 64, 2, 4, 2, 2, 0, 4> T256_k64_s2_w8_l4;
 typedef TileShape<256, 256, 32, 2, 2, 5, 1, 4> T256_k32_s5_w4_e4;
+typedef TileShape<256, 256, 64, 2, 2, 2, 1, 0, 0, 1, 16> T256_k64_s2_w4_mi16;
+typedef TileShape<256, 256, 64, 2, 4, 2, 2, 0, 0, 1, 16> T256_k64_s2_w8_mi16;
+typedef TileShape<256, 256, 32, 2, 4, 4, 2, 0, 0, 1, 16> T256_k32_s4_w8_mi16;
+typedef TileShape<256, 256, 64, 4, 2, 2, 2, 0, 0, 1, 16> T256_k64_s2_w8x_mi16;
+typedef TileShape<256, 256, 64, 2, 4, 2, 2, 0, 4, 1, 16> T256_k64_s2_w8_l4_mi16;
+typedef TileShape<256, 128, 64, 2, 2, 3, 1, 0, 0, 1, 16> T256x128_k64_s3_w4_mi16;
+typedef TileShape<256, 128, 64, 2, 4, 3, 2, 0, 0, 1, 16> T256x128_k64_s3_w8_mi16;
+typedef TileShape<128, 128, 64, 2, 2, 3, 1, 0, 0, 1, 16> T128_k64_s3_w4_mi16;
+typedef TileShape<128, 128, 64, 2, 4, 3, 2, 0, 0, 1, 16> T128_k64_s3_w8_mi16;
+typedef TileShape<64, 64, 64, 2, 2, 3, 2, 0, 0, 1, 16> T64_k64_s3_w4_mi16;
 typedef TileShape<256, 128, 64, 2, 2, 3, 1> T256x128_k64_s3_w4;
 typedef TileShape<128, 128, 64, 2, 2, 3, 1> T128_k64_s3_w4;
 typedef TileShape<64, 64, 64, 2, 2, 3, 2> T64_k64_s3_w4;
@@ -1356,6 +1395,16 @@ constexpr Variant kVariants[] = {
     {"mfma32_256x256x32_w8_s4_d2", 256, 256, 8, launch_mfma<T256_k32_s4_w8_d2>},
     {"mfma32_256x256x64_w8_s2_l4", 256, 256, 8, launch_mfma<T256_k64_s2_w8_l4>},
     {"mfma32_256x256x32_w4_s5_e4", 256, 256, 8, launch_mfma<T256_k32_s5_w4_e4>},
+    {"mfma16_256x256x64_w4_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w4_mi16>},
+    {"mfma16_256x256x64_w8_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8_mi16>},
+    {"mfma16_256x256x32_w8_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w8_mi16>},
+    {"mfma16_256x256x64_w8x_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8x_mi16>},
+    {"mfma16_256x256x64_w8_s2_l4", 256, 256, 8, launch_mfma<T256_k64_s2_w8_l4_mi16>},
+    {"mfma16_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4_mi16>},
+    {"mfma16_256x128x64_w8_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w8_mi16>},
+    {"mfma16_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4_mi16>},
+    {"mfma16_128x128x64_w8_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w8_mi16>},
+    {"mfma16_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4_mi16>},
     {"mfma32_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4>},
     {"mfma32_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4>},
     {"mfma32_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4>},
@@ -1422,13 +1471,13 @@ struct Candidate {
 constexpr int kCUs = 256;
 constexpr double kWaveCostUs = 3.0;
 constexpr Candidate kCandidates[] = {
-    {variant_index("mfma32_256x256x64_w8_s2"), 256, 256, 1100.0},
-    {variant_index("mfma32_256x128x64_w4_s3"), 256, 128, 1000.0},
-    {variant_index("mfma32_128x128x64_w4_s3"), 128, 128, 900.0},
-    {variant_index("mfma32_64x64x64_w4_s3"), 64, 64, 650.0},
+    {variant_index("mfma16_256x256x64_w8_s2_l4"), 256, 256, 1230.0},
+    {variant_index("mfma16_256x128x64_w8_s3"), 256, 128, 1040.0},
+    {variant_index("mfma16_128x128x64_w8_s3"), 128, 128, 900.0},
+    {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 650.0},
 };
-static_assert(variant_index("mfma32_256x256x64_w8_s2") >= 0 && variant_index("mfma32_256x128x64_w4_s3") >= 0 &&
-                  variant_index("mfma32_128x128x64_w4_s3") >= 0 && variant_index("mfma32_64x64x64_w4_s3") >= 0,
+static_assert(variant_index("mfma16_256x256x64_w8_s2_l4") >= 0 && variant_index("mfma16_256x128x64_w8_s3") >= 0 &&
+                  variant_index("mfma16_128x128x64_w8_s3") >= 0 && variant_index("mfma16_64x64x64_w4_s3") >= 0,
               "selected variants are in the table");
 
 int select_mfma(int64_t M, int64_t N, int64_t K)
