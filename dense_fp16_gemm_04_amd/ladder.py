@@ -37,18 +37,29 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# What each variant changes, relative to the default (mfma32_256x256x64_w8_s2).
+# What each variant changes.  mfma32 variants use v_mfma_f32_32x32x16_f16,
+# mfma16 ones v_mfma_f32_16x16x32_f16.
 RUNGS = {
     "simple_f32_per_element": "one thread per output, no tiling (the naive baseline)",
     "mfma32_64x64x64_w4_s3": "64x64 tile, 4 waves, 3-stage ring",
     "mfma32_128x128x64_w4_s3": "128x128 tile: 2x the reuse per loaded byte",
     "mfma32_256x128x64_w4_s3": "256x128 tile",
     "mfma32_256x256x64_w4_s2": "256x256 tile, 4 waves (1 per SIMD, 256 accumulators each), 2 stages",
-    "mfma32_256x256x64_w8_s2": "256x256 tile, 8 waves (2 per SIMD, 128 accumulators each): the default",
+    "mfma32_256x256x64_w8_s2": "256x256 tile, 8 waves (2 per SIMD, 128 accumulators each)",
     "mfma32_256x256x32_w8_s5": "same, BK 32 with a 5-stage ring (loads 4 steps ahead)",
     "mfma32_256x256x32_w8_s4_d2": "BK 32, 4 stages, fragments read a whole step ahead, loads spread over the step",
     "mfma32_256x256x64_w8_s2_l4": "only 4 of the 8 waves issue global->LDS loads (a producer/consumer split)",
     "mfma32_256x256x32_w4_s5_e4": "4 waves, BK 32, 5 stages, half of each step's loads issued a step early",
+    "mfma16_256x256x64_w4_s2": "16x16x32 MFMAs, 4 waves (1 per SIMD, 128x128 each)",
+    "mfma16_256x256x64_w8_s2": "16x16x32 MFMAs, 8 waves (2 per SIMD, 128x64 each)",
+    "mfma16_256x256x32_w8_s4": "16x16x32 MFMAs, 8 waves, BK 32 with a 4-stage ring",
+    "mfma16_256x256x64_w8x_s2": "16x16x32 MFMAs, 8 waves laid out 4x2 (64x128 each)",
+    "mfma16_256x256x64_w8_s2_l4": "16x16x32 MFMAs, 8 waves, 4 of them loading: the default",
+    "mfma16_256x128x64_w4_s3": "16x16x32 MFMAs, 256x128 tile, 4 waves",
+    "mfma16_256x128x64_w8_s3": "16x16x32 MFMAs, 256x128 tile, 8 waves (default for one GPU's share)",
+    "mfma16_128x128x64_w4_s3": "16x16x32 MFMAs, 128x128 tile, 4 waves",
+    "mfma16_128x128x64_w8_s3": "16x16x32 MFMAs, 128x128 tile, 8 waves (default for mid sizes)",
+    "mfma16_64x64x64_w4_s3": "16x16x32 MFMAs, 64x64 tile (default for small sizes)",
     "mfma32_256x256x64_w4_stream": "persistent grid: the ring runs on across tile boundaries",
     "mfma32_256x256x64_w4_asm": "persistent grid with a hand-scheduled (inline asm) main loop",
     "mfma32_256x256x32_w4_s5_split": "hand-scheduled, loads split between MFMA rows, 5-stage BK-32 ring",
