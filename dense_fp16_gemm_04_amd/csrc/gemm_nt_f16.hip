@@ -29,11 +29,15 @@
 //
 // LDS layout of one stage: the A tile (BM rows) then the B tile (BN rows);
 // each row holds BK fp16 (64 or 128 bytes) as 16-byte chunks.  gfx950's LDS
-// serves 64 banks x 4 bytes per cycle, so the 16 lanes of a 16-byte read
-// must hit 16 different 16-byte bank groups: chunk c of row r is stored at
-// position c ^ ((r / ROWS_PER_LINE) % CHUNKS), ROWS_PER_LINE being the rows
-// that share one 256-byte line.  Reads of 16 consecutive rows at one logical
-// chunk are then conflict-free (measured: zero bank conflicts).
+// serves 64 banks x 4 bytes per cycle; a 16-byte read (ds_read_b128) takes
+// four passes of 16 lanes, and the lanes of one pass must hit 16 different
+// 16-byte bank groups.  The passes are lanes {0-3, 12-15, 20-23, 24-27},
+// {4-11, 16-19, 28-31} and the same plus 32 (measured with a probe that
+// puts two lanes on one bank and reads SQ_LDS_BANK_CONFLICT).  Chunk c of
+// row r is stored at position c ^ ((r / ROWS_PER_LINE) % CHUNKS),
+// ROWS_PER_LINE being the rows that share one 256-byte line, which makes
+// every fragment read conflict-free except 64-byte rows under 16x16x32
+// MFMAs, which get their own XOR term (swz).
 //
 // Matrix-core step: v_mfma_f32_32x32x16_f16.  Operand lane l holds 8
 // consecutive-k fp16 values of row (l % 32), k offset 8 * (l / 32); the same
@@ -227,7 +231,22 @@ struct Int {
 template <class T>
 __device__ __forceinline__ int swz(int row, int chunk)
 {
+    // 64-byte rows read by 16x16x32 MFMAs (lane l: row l % 16, chunk
+    // l / 16): one LDS pass serves lanes {0-3, 12-15, 20-23, 24-27}, i.e.
+    // rows 0-3 and 12-15 at chunk 0 with rows 4-11 at chunk 1 (and likewise
+    // for the other passes), so the row-quad term must split quads {0, 3}
+    // from {1, 2}: XOR with 2 * ((row / 8) % 2) does, the default XOR with
+    // (row / 4) % 4 puts half of each pass on the same banks.
+    if constexpr (T::CHUNKS == 4 && T::MI == 16) return chunk ^ (((row >> 3) & 1) << 1);
     return chunk ^ ((row >> T::SWZ_SHIFT) & (T::CHUNKS - 1));
+}
+
+// acc += b * a (v_mfma_f32_16x16x32_f16) with the accumulator held in AGPRs.
+// The memory clobber keeps every LDS and global access on its side of the
+// MFMA, so the source order of a loop built from these is its issue order.
+__device__ __forceinline__ void mfma16_agpr(float4_t& acc, const half8_t& b, const half8_t& a)
+{
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a) : "memory");
 }
 
 // Epilogue: fp32 -> fp16 (round to nearest even) and store.  In each MFMA
@@ -437,6 +456,10 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
         for (int j = 0; j < T::FN; ++j) fb[set_of(p, kk)][j] = *(const half8_t*)(pb + j * T::MI * T::ROW_BYTES);
     };
 
+    // When the accumulators fill all 256 AGPRs (one wave per SIMD, 16x16
+    // blocks), MFMAs compiled from the builtin get their accumulators moved
+    // between AGPRs and VGPRs inside the loop; asm MFMAs keep them in place.
+    constexpr bool kAgprAcc = T::MI == 16 && T::OCC == 1 && T::FM * T::FN * T::ACC == 256;
     auto mma = [&](int p, int kk) {
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
@@ -445,6 +468,8 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                 if constexpr (T::MI == 32)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[set_of(p, kk)][j], fa[set_of(p, kk)][i],
                                                                        acc[i][j], 0, 0, 0);
+                else if constexpr (kAgprAcc)
+                    mfma16_agpr(acc[i][j], fb[set_of(p, kk)][j], fa[set_of(p, kk)][i]);
                 else
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[set_of(p, kk)][j], fa[set_of(p, kk)][i],
                                                                        acc[i][j], 0, 0, 0);
@@ -557,11 +582,167 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
         // no global->LDS load may still be writing when the workgroup ends
         // (nor when the ring is reused for the epilogue below)
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        // asm MFMAs are opaque to the compiler's hazard checks: let the last
+        // ones write their accumulators before they are read
+        if constexpr (kAgprAcc) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     }
 
     // Small tiles (64 x 64) keep the direct stores: their epilogue is short
     // and the two extra barriers cost more than the wider stores save.
     if (T::BM * T::BN >= 128 * 128 && c_vec == 2) {
+        __syncthreads();  // every wave is done with the ring
+        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem);
+    } else {
+        epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
+    }
+}
+
+// One wave per SIMD, every instruction of the K loop in a fixed order.
+//
+// Four waves each own a 128 x 128 quarter of the 256 x 256 tile: 8 x 8
+// blocks of 16 x 16, 256 accumulator floats per lane, every AGPR.  With one
+// wave per SIMD nothing else issues while this wave waits, so stalls cannot
+// be covered by a partner wave as in the 8-wave kernel; instead nothing is
+// bunched.  A BK = 64 step is two sub-steps of 32 k (64 MFMAs each):
+//   sub-step 0: its MFMAs, and after every RS-th of them one fragment read
+//               of sub-step 1 (16 reads);
+//   barrier:    this wave's loads of step ks + 1 have landed (vmcnt(0)), its
+//               reads of sub-step 1 have returned; every wave is done with
+//               this step's stage;
+//   sub-step 1: its MFMAs, with one fragment read of the next step's
+//               sub-step 0 after every RS-th, and one of this wave's 16
+//               global->LDS loads of step ks + 2 (into this step's stage)
+//               after every LS-th, starting half-way into the first LS.
+// The MFMAs are asm statements (mfma16_agpr), which keeps the accumulators
+// in place: compiled from the builtin, a kernel whose accumulators fill all
+// 256 AGPRs moves them between AGPRs and VGPRs inside the loop (1.3 copies
+// per MFMA).  The fragments are read in the order the MFMAs first need them
+// (A block 0, B blocks 0 .. 7, A blocks 1 .. 7), so the compiler's lgkmcnt
+// waits before each MFMA only cover reads issued long before.
+template <class T, int RS, int LS>
+__global__ void __launch_bounds__(T::THREADS, 1)
+gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
+                    _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+                    int group_m, int c_vec)
+{
+    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && T::STAGES == 2 && T::LOADERS == T::WAVES &&
+                      T::OCC == 1,
+                  "16x16x32 MFMAs, two sub-steps per step, two stages, every wave loads");
+    constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
+    constexpr int R = T::FM + T::FN;  // fragment reads per sub-step
+    static_assert(RS * (R - 1) < G && LS * (T::LOADS - 1) + LS / 2 < G, "reads and loads fit in a sub-step");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    const int rows_a = min(T::BM, M - m0), rows_b = min(T::BN, N - n0);
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * row_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * row_bytes);
+
+    // Load l < A_LOADS fills KiB (wave * A_LOADS + l) of the stage's A tile,
+    // the others KiB (wave * B_LOADS + l - A_LOADS) of its B tile; lane
+    // placement and swizzle as in gemm_nt_f16_mfma.
+    const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
+    uint32_t voff[T::LOADS];
+    int kc[T::LOADS];  // first k of the fetched chunk
+#pragma unroll
+    for (int l = 0; l < T::LOADS; ++l) {
+        const bool is_a = l < T::A_LOADS;
+        const int row = (wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? l : l - T::A_LOADS)) * T::ROWS_PER_LOAD +
+                        ld_r;
+        const int c = swz<T>(row, ld_p);
+        voff[l] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
+        kc[l] = c * 8;
+    }
+    auto issue_load = [&](int stage, int kstep, int l) __attribute__((always_inline)) {
+        const int k0 = kstep * T::BK;
+        const uint32_t v = kc[l] < K - k0 ? voff[l] : kOob;  // chunks at or past K read as zero
+        const uint32_t soff = (uint32_t)k0 * 2u;
+        unsigned char* st = smem + stage * T::STAGE_BYTES;
+        if (l < T::A_LOADS)  // (a buffer resource cannot be the result of ?:)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st + (wave * T::A_LOADS + l) * 1024), 16, v,
+                                                     soff, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void_t*)(st + T::A_BYTES + (wave * T::B_LOADS + l - T::A_LOADS) * 1024), 16, v, soff, 0, 0);
+    };
+
+    const int fr_row = lane % T::MI;
+    const int fr_hi = lane / T::MI;
+    const int a_row0 = wm * T::WTM + fr_row;
+    const int b_row0 = wn * T::WTN + fr_row;
+    int fr_pos[T::KK];
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, T::CPS * kk + fr_hi) * 16;
+
+    // Fragment set kk holds sub-step kk of the current step.
+    half8_t fa[2][T::FM], fb[2][T::FN];
+    typename T::acc_t acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < T::ACC; ++r) acc[i][j][r] = 0.0f;
+
+    auto read_one = [&](int set, const unsigned char* base, int idx) __attribute__((always_inline)) {
+        const unsigned char* pa = base + a_row0 * T::ROW_BYTES + fr_pos[set];
+        const unsigned char* pb = base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[set];
+        if (idx == 0)
+            fa[set][0] = *(const half8_t*)pa;
+        else if (idx <= T::FN)
+            fb[set][idx - 1] = *(const half8_t*)(pb + (idx - 1) * T::MI * T::ROW_BYTES);
+        else
+            fa[set][idx - T::FN] = *(const half8_t*)(pa + (idx - T::FN) * T::MI * T::ROW_BYTES);
+    };
+    // MFMAs of sub-step `cs` (block row i = t / FN, column j = t % FN), with
+    // the reads of sub-step 1 - cs from `rbase` and, if LD, the loads of
+    // step `lstep` into `lstage` interleaved.
+    auto substep = [&](int cs, const unsigned char* rbase, auto ld, int lstage, int lstep)
+                       __attribute__((always_inline)) {
+        constexpr bool LD = decltype(ld)::value;
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+            mfma16_agpr(acc[t / T::FN][t % T::FN], fb[cs][t % T::FN], fa[cs][t / T::FN]);
+            if (t % RS == 0 && t / RS < R) read_one(1 - cs, rbase, t / RS);
+            if constexpr (LD)
+                if (t % LS == LS / 2 && t / LS < T::LOADS) issue_load(lstage, lstep, t / LS);
+        }
+    };
+
+    const int nk = (K + T::BK - 1) / T::BK;
+    if (nk > 0) {
+#pragma unroll
+        for (int l = 0; l < T::LOADS; ++l) issue_load(0, 0, l);
+        lds_barrier<0>();
+#pragma unroll
+        for (int l = 0; l < T::LOADS; ++l) issue_load(1, 1, l);
+#pragma unroll
+        for (int idx = 0; idx < R; ++idx) read_one(0, smem, idx);
+        int cur = 0;
+        for (int ks = 0; ks < nk; ++ks) {
+            // steps past the end of K load zeros into stages never read
+            substep(0, smem + cur * T::STAGE_BYTES, Flag<false>{}, 0, 0);
+            lds_barrier<0>();
+            substep(1, smem + (cur ^ 1) * T::STAGE_BYTES, Flag<true>{}, cur, ks + 2);
+            cur ^= 1;
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        // The compiler cannot see that the asm statements are MFMAs: give
+        // the last ones time to write their accumulators before they are
+        // read (the longest MFMA-write to read hazard is under 24 wait
+        // states).
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    }
+
+    if (c_vec == 2) {
         __syncthreads();  // every wave is done with the ring
         epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem);
     } else {
@@ -1308,6 +1489,19 @@ int launch_mfma(const void* A, const void* B, void* C, int64_t M, int64_t N, int
     return (int)hipGetLastError();
 }
 
+template <class T, int RS, int LS>
+int launch_ordered(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int group_m,
+                   hipStream_t stream)
+{
+    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
+    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
+    const int c_vec = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 2 : ((N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0);
+    hipLaunchKernelGGL((gemm_nt_f16_ordered<T, RS, LS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0,
+                       stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N, (int)K,
+                       (int)tiles_m, (int)tiles_n, group_m, c_vec);
+    return (int)hipGetLastError();
+}
+
 int num_cus(int device)
 {
     static int cache[64];
@@ -1400,6 +1594,7 @@ constexpr Variant kVariants[] = {
     {"mfma16_256x256x32_w8_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w8_mi16>},
     {"mfma16_256x256x64_w8x_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8x_mi16>},
     {"mfma16_256x256x64_w8_s2_l4", 256, 256, 8, launch_mfma<T256_k64_s2_w8_l4_mi16>},
+    {"mfma16_256x256x64_w4_s2_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w4_mi16, 4, 4>},
     {"mfma16_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4_mi16>},
     {"mfma16_256x128x64_w8_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w8_mi16>},
     {"mfma16_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4_mi16>},
@@ -1455,28 +1650,34 @@ constexpr int variant_index(const char* name)
     return -1;
 }
 
-// Shape -> variant.  Four tile sizes compete; each is priced as
+// Shape -> variant.  Five kernels (four tile sizes) compete; each is priced
+// as
 //   ceil(tiles / 256 CUs) x (tile flops / per-CU rate + fixed cost),
 // i.e. whole waves of tiles over the chip (one workgroup per CU), with the
 // per-CU rate each kernel sustains on a full chip (measured on MI355X at
 // 4096^3 .. 8192^3, fp16 random data) and a fixed per-wave cost for launch,
 // pipeline fill and epilogue.  Small problems then take small tiles (more
-// CUs busy), large ones the 256 x 256 kernel (most reuse per byte loaded).
+// CUs busy), large ones a 256 x 256 kernel (most reuse per byte loaded).
+// Of the two 256 x 256 kernels the 4-wave hand-ordered one has the higher
+// rate and the 8-wave one the shorter fill and epilogue, which wins when K
+// is short (4096 x 4096 x 1024: 34.3 against 35.6 us).
 struct Candidate {
     int variant;
     int bm, bn;
     double tflops_chip;  // sustained on a full chip
+    double wave_us;      // fixed cost per wave of tiles
 };
 
 constexpr int kCUs = 256;
-constexpr double kWaveCostUs = 3.0;
 constexpr Candidate kCandidates[] = {
-    {variant_index("mfma16_256x256x64_w8_s2_l4"), 256, 256, 1230.0},
-    {variant_index("mfma16_256x128x64_w8_s3"), 256, 128, 1040.0},
-    {variant_index("mfma16_128x128x64_w8_s3"), 128, 128, 900.0},
-    {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 650.0},
+    {variant_index("mfma16_256x256x64_w4_s2_ordered"), 256, 256, 1290.0, 5.5},
+    {variant_index("mfma16_256x256x64_w8_s2_l4"), 256, 256, 1230.0, 3.0},
+    {variant_index("mfma16_256x128x64_w8_s3"), 256, 128, 1040.0, 3.0},
+    {variant_index("mfma16_128x128x64_w8_s3"), 128, 128, 900.0, 3.0},
+    {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 650.0, 3.0},
 };
-static_assert(variant_index("mfma16_256x256x64_w8_s2_l4") >= 0 && variant_index("mfma16_256x128x64_w8_s3") >= 0 &&
+static_assert(variant_index("mfma16_256x256x64_w4_s2_ordered") >= 0 &&
+                  variant_index("mfma16_256x256x64_w8_s2_l4") >= 0 && variant_index("mfma16_256x128x64_w8_s3") >= 0 &&
                   variant_index("mfma16_128x128x64_w8_s3") >= 0 && variant_index("mfma16_64x64x64_w4_s3") >= 0,
               "selected variants are in the table");
 
@@ -1489,7 +1690,7 @@ int select_mfma(int64_t M, int64_t N, int64_t K)
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         const int64_t waves = (tiles + kCUs - 1) / kCUs;
         const double tile_us = 2.0 * c.bm * c.bn * (double)K / (c.tflops_chip * 1e12 / kCUs) * 1e6;
-        const double us = (double)waves * (tile_us + kWaveCostUs);
+        const double us = (double)waves * (tile_us + c.wave_us);
         if (first || us < best_us) {
             best = c.variant;
             best_us = us;

@@ -50,11 +50,12 @@ RUNGS = {
     "mfma32_256x256x32_w8_s4_d2": "BK 32, 4 stages, fragments read a whole step ahead, loads spread over the step",
     "mfma32_256x256x64_w8_s2_l4": "only 4 of the 8 waves issue global->LDS loads (a producer/consumer split)",
     "mfma32_256x256x32_w4_s5_e4": "4 waves, BK 32, 5 stages, half of each step's loads issued a step early",
-    "mfma16_256x256x64_w4_s2": "16x16x32 MFMAs, 4 waves (1 per SIMD, 128x128 each)",
+    "mfma16_256x256x64_w4_s2": "16x16x32 MFMAs, 4 waves (1 per SIMD, 128x128 each, accumulators in all 256 AGPRs)",
     "mfma16_256x256x64_w8_s2": "16x16x32 MFMAs, 8 waves (2 per SIMD, 128x64 each)",
     "mfma16_256x256x32_w8_s4": "16x16x32 MFMAs, 8 waves, BK 32 with a 4-stage ring",
     "mfma16_256x256x64_w8x_s2": "16x16x32 MFMAs, 8 waves laid out 4x2 (64x128 each)",
-    "mfma16_256x256x64_w8_s2_l4": "16x16x32 MFMAs, 8 waves, 4 of them loading: the default",
+    "mfma16_256x256x64_w8_s2_l4": "16x16x32 MFMAs, 8 waves, 4 of them loading (default when K is short)",
+    "mfma16_256x256x64_w4_s2_ordered": "4 waves again, every read and load placed by hand, one per 4 MFMAs: the default",
     "mfma16_256x128x64_w4_s3": "16x16x32 MFMAs, 256x128 tile, 4 waves",
     "mfma16_256x128x64_w8_s3": "16x16x32 MFMAs, 256x128 tile, 8 waves (default for one GPU's share)",
     "mfma16_128x128x64_w4_s3": "16x16x32 MFMAs, 128x128 tile, 4 waves",
