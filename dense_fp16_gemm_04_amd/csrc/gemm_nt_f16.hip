@@ -599,35 +599,39 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 
 // One wave per SIMD, every instruction of the K loop in a fixed order.
 //
-// Four waves each own a 128 x 128 quarter of the 256 x 256 tile: 8 x 8
-// blocks of 16 x 16, 256 accumulator floats per lane, every AGPR.  With one
-// wave per SIMD nothing else issues while this wave waits, so stalls cannot
-// be covered by a partner wave as in the 8-wave kernel; instead nothing is
-// bunched.  A BK = 64 step is two sub-steps of 32 k (64 MFMAs each):
+// Four waves each own a quarter of the tile (for 256 x 256: 128 x 128, i.e.
+// 8 x 8 blocks of 16 x 16 and 256 accumulator floats per lane, every AGPR).
+// With one wave per SIMD nothing else issues while this wave waits, so
+// stalls cannot be covered by a partner wave as in the 8-wave kernel;
+// instead nothing is bunched.  A BK = 64 step is two sub-steps of 32 k
+// (FM x FN MFMAs each):
 //   sub-step 0: its MFMAs, and after every RS-th of them one fragment read
-//               of sub-step 1 (16 reads);
-//   barrier:    this wave's loads of step ks + 1 have landed (vmcnt(0)), its
-//               reads of sub-step 1 have returned; every wave is done with
-//               this step's stage;
+//               of sub-step 1;
+//   barrier:    this wave's loads of step ks + 1 have landed (vmcnt: only
+//               the loads of the STAGES - 2 later steps may still be in
+//               flight), its reads of sub-step 1 have returned; every wave
+//               is done with this step's stage;
 //   sub-step 1: its MFMAs, with one fragment read of the next step's
-//               sub-step 0 after every RS-th, and one of this wave's 16
-//               global->LDS loads of step ks + 2 (into this step's stage)
-//               after every LS-th, starting half-way into the first LS.
+//               sub-step 0 after every RS-th, and one of this wave's
+//               global->LDS loads of step ks + STAGES (into this step's
+//               stage) after every LS-th, starting half-way into the first.
 // The MFMAs are asm statements (mfma16_agpr), which keeps the accumulators
 // in place: compiled from the builtin, a kernel whose accumulators fill all
 // 256 AGPRs moves them between AGPRs and VGPRs inside the loop (1.3 copies
 // per MFMA).  The fragments are read in the order the MFMAs first need them
-// (A block 0, B blocks 0 .. 7, A blocks 1 .. 7), so the compiler's lgkmcnt
-// waits before each MFMA only cover reads issued long before.
+// (A block 0, B blocks 0 .. FN-1, A blocks 1 .. FM-1), so the compiler's
+// lgkmcnt waits before each MFMA only cover reads issued long before.  Loads
+// of steps that lie wholly inside K skip the per-lane K check.
 template <class T, int RS, int LS>
 __global__ void __launch_bounds__(T::THREADS, 1)
 gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                     _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
                     int group_m, int c_vec)
 {
-    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && T::STAGES == 2 && T::LOADERS == T::WAVES &&
-                      T::OCC == 1,
-                  "16x16x32 MFMAs, two sub-steps per step, two stages, every wave loads");
+    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && T::LOADERS == T::WAVES && T::OCC == 1 &&
+                      T::WAVES == 4,
+                  "16x16x32 MFMAs, two sub-steps per step, four waves, every wave loads");
+    constexpr int S = T::STAGES;
     constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
     constexpr int R = T::FM + T::FN;  // fragment reads per sub-step
     static_assert(RS * (R - 1) < G && LS * (T::LOADS - 1) + LS / 2 < G, "reads and loads fit in a sub-step");
@@ -661,9 +665,11 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
         voff[l] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
         kc[l] = c * 8;
     }
-    auto issue_load = [&](int stage, int kstep, int l) __attribute__((always_inline)) {
+    // MASKED: the step may reach past K (chunks at or past K read as zero)
+    auto issue_load = [&](int stage, int kstep, int l, auto masked) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked)::value;
         const int k0 = kstep * T::BK;
-        const uint32_t v = kc[l] < K - k0 ? voff[l] : kOob;  // chunks at or past K read as zero
+        const uint32_t v = (!MASKED || kc[l] < K - k0) ? voff[l] : kOob;
         const uint32_t soff = (uint32_t)k0 * 2u;
         unsigned char* st = smem + stage * T::STAGE_BYTES;
         if (l < T::A_LOADS)  // (a buffer resource cannot be the result of ?:)
@@ -705,7 +711,7 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
     // MFMAs of sub-step `cs` (block row i = t / FN, column j = t % FN), with
     // the reads of sub-step 1 - cs from `rbase` and, if LD, the loads of
     // step `lstep` into `lstage` interleaved.
-    auto substep = [&](int cs, const unsigned char* rbase, auto ld, int lstage, int lstep)
+    auto substep = [&](int cs, const unsigned char* rbase, auto ld, int lstage, int lstep, auto masked)
                        __attribute__((always_inline)) {
         constexpr bool LD = decltype(ld)::value;
 #pragma unroll
@@ -713,27 +719,34 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
             mfma16_agpr(acc[t / T::FN][t % T::FN], fb[cs][t % T::FN], fa[cs][t / T::FN]);
             if (t % RS == 0 && t / RS < R) read_one(1 - cs, rbase, t / RS);
             if constexpr (LD)
-                if (t % LS == LS / 2 && t / LS < T::LOADS) issue_load(lstage, lstep, t / LS);
+                if (t % LS == LS / 2 && t / LS < T::LOADS) issue_load(lstage, lstep, t / LS, masked);
         }
     };
 
     const int nk = (K + T::BK - 1) / T::BK;
     if (nk > 0) {
 #pragma unroll
-        for (int l = 0; l < T::LOADS; ++l) issue_load(0, 0, l);
-        lds_barrier<0>();
+        for (int s = 0; s < S - 1; ++s)
 #pragma unroll
-        for (int l = 0; l < T::LOADS; ++l) issue_load(1, 1, l);
+            for (int l = 0; l < T::LOADS; ++l) issue_load(s, s, l, Flag<true>{});
+        lds_barrier<T::LOADS * (S - 2)>();
+#pragma unroll
+        for (int l = 0; l < T::LOADS; ++l) issue_load(S - 1, S - 1, l, Flag<true>{});
 #pragma unroll
         for (int idx = 0; idx < R; ++idx) read_one(0, smem, idx);
-        int cur = 0;
-        for (int ks = 0; ks < nk; ++ks) {
+        int cur = 0;  // stage of step ks
+        auto step = [&](int ks, auto masked) __attribute__((always_inline)) {
+            const int nxt = cur + 1 == S ? 0 : cur + 1;
+            substep(0, smem + cur * T::STAGE_BYTES, Flag<false>{}, 0, 0, masked);
+            lds_barrier<T::LOADS * (S - 2)>();
             // steps past the end of K load zeros into stages never read
-            substep(0, smem + cur * T::STAGE_BYTES, Flag<false>{}, 0, 0);
-            lds_barrier<0>();
-            substep(1, smem + (cur ^ 1) * T::STAGE_BYTES, Flag<true>{}, cur, ks + 2);
-            cur ^= 1;
-        }
+            substep(1, smem + nxt * T::STAGE_BYTES, Flag<true>{}, cur, ks + S, masked);
+            cur = nxt;
+        };
+        const int nfull = K / T::BK;  // steps that lie wholly inside K
+        int ks = 0;
+        for (; ks < nk && ks + S < nfull; ++ks) step(ks, Flag<false>{});
+        for (; ks < nk; ++ks) step(ks, Flag<true>{});
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         // The compiler cannot see that the asm statements are MFMAs: give
         // the last ones time to write their accumulators before they are
@@ -1595,6 +1608,7 @@ constexpr Variant kVariants[] = {
     {"mfma16_256x256x64_w8x_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8x_mi16>},
     {"mfma16_256x256x64_w8_s2_l4", 256, 256, 8, launch_mfma<T256_k64_s2_w8_l4_mi16>},
     {"mfma16_256x256x64_w4_s2_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w4_mi16, 4, 4>},
+    {"mfma16_256x128x64_w4_s3_ordered", 256, 128, 8, launch_ordered<T256x128_k64_s3_w4_mi16, 2, 2>},
     {"mfma16_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4_mi16>},
     {"mfma16_256x128x64_w8_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w8_mi16>},
     {"mfma16_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4_mi16>},
@@ -1672,12 +1686,13 @@ constexpr int kCUs = 256;
 constexpr Candidate kCandidates[] = {
     {variant_index("mfma16_256x256x64_w4_s2_ordered"), 256, 256, 1290.0, 5.5},
     {variant_index("mfma16_256x256x64_w8_s2_l4"), 256, 256, 1230.0, 3.0},
-    {variant_index("mfma16_256x128x64_w8_s3"), 256, 128, 1040.0, 3.0},
+    {variant_index("mfma16_256x128x64_w4_s3_ordered"), 256, 128, 1100.0, 3.0},
     {variant_index("mfma16_128x128x64_w8_s3"), 128, 128, 900.0, 3.0},
     {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 650.0, 3.0},
 };
 static_assert(variant_index("mfma16_256x256x64_w4_s2_ordered") >= 0 &&
-                  variant_index("mfma16_256x256x64_w8_s2_l4") >= 0 && variant_index("mfma16_256x128x64_w8_s3") >= 0 &&
+                  variant_index("mfma16_256x256x64_w8_s2_l4") >= 0 &&
+                  variant_index("mfma16_256x128x64_w4_s3_ordered") >= 0 &&
                   variant_index("mfma16_128x128x64_w8_s3") >= 0 && variant_index("mfma16_64x64x64_w4_s3") >= 0,
               "selected variants are in the table");
 

@@ -70,8 +70,8 @@ def test_selection(lib):
     assert name(1024, 1024, 1024) == "mfma16_64x64x64_w4_s3"
     assert name(256, 256, 256) == "mfma16_64x64x64_w4_s3"
     # one GPU's share of an 8192^3 product split eight ways along M or N
-    assert name(1024, 8192, 8192) == "mfma16_256x128x64_w8_s3"
-    assert name(8192, 1024, 8192) == "mfma16_256x128x64_w8_s3"
+    assert name(1024, 8192, 8192) == "mfma16_256x128x64_w4_s3_ordered"
+    assert name(8192, 1024, 8192) == "mfma16_256x128x64_w4_s3_ordered"
     # K not a multiple of 8 cannot use the MFMA kernels
     assert binding.gemm_nt_f16_config_name(64, 64, 7).startswith("simple")
     assert lib.gemm_nt_f16_select(-1, 4, 4) == -1
