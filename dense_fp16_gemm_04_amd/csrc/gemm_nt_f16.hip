@@ -509,11 +509,21 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     // steps, so the fragment set parity is known at compile time.
     auto main_loop = [&](auto tag) {
         constexpr bool LD = decltype(tag)::value;
+        if constexpr (T::EARLY == 0) {
+            // every stage is free at the start: fill them all, then wait
+            // for step 0 only
 #pragma unroll
-        for (int s = 0; s < T::STAGES - 1; ++s)
-            if constexpr (LD) issue_loads(s, s);
-        lds_barrier<T::LOADS * (T::STAGES - 2)>();
-        if constexpr (LD) issue_load_range(T::STAGES - 1, T::STAGES - 1, 0, T::LATE);
+            for (int s = 0; s < T::STAGES; ++s)
+                if constexpr (LD) issue_loads(s, s);
+            lds_barrier<T::LOADS * (T::STAGES - 1)>();
+        } else {
+            // the early part of step STAGES - 1 goes out during step 0
+#pragma unroll
+            for (int s = 0; s < T::STAGES - 1; ++s)
+                if constexpr (LD) issue_loads(s, s);
+            lds_barrier<T::LOADS * (T::STAGES - 2)>();
+            if constexpr (LD) issue_load_range(T::STAGES - 1, T::STAGES - 1, 0, T::LATE);
+        }
 #pragma unroll
         for (int kk = 0; kk < T::DIST; ++kk) read_frags(0, smem, kk);
 
@@ -725,13 +735,13 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
 
     const int nk = (K + T::BK - 1) / T::BK;
     if (nk > 0) {
+        // every stage is free at the start: fill them all, then wait for
+        // step 0 only
 #pragma unroll
-        for (int s = 0; s < S - 1; ++s)
+        for (int s = 0; s < S; ++s)
 #pragma unroll
             for (int l = 0; l < T::LOADS; ++l) issue_load(s, s, l, Flag<true>{});
-        lds_barrier<T::LOADS * (S - 2)>();
-#pragma unroll
-        for (int l = 0; l < T::LOADS; ++l) issue_load(S - 1, S - 1, l, Flag<true>{});
+        lds_barrier<T::LOADS * (S - 1)>();
 #pragma unroll
         for (int idx = 0; idx < R; ++idx) read_one(0, smem, idx);
         int cur = 0;  // stage of step ks
