@@ -32,7 +32,7 @@ PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 # WRITE_SIZE x 1.000, the factors read off a plain 1 GiB device copy) for one
 # kernel on one workload.  Reported only for that pair; reset to None when the
 # kernel changes.
-TRAFFIC = {"workload": "square_8192", "kernel": "mfma16_256x256x64_w4_s2_ordered", "bytes": 1.759e9}
+TRAFFIC = {"workload": "square_8192", "kernel": "mfma16_256x256x64_w4_s2_ordered", "bytes": 1.752e9}
 
 
 def log(*a):
@@ -80,6 +80,9 @@ def main(argv=None) -> int:
     p.add_argument("--cooldown", type=float, default=3.0, help="seconds idle before the timed window")
     p.add_argument("--cpu-rows", type=int, default=8192,
                    help="rows of A in the oracle's timed slab (0 skips the CPU baseline)")
+    p.add_argument("--throttle-check", type=int, default=100, metavar="N",
+                   help="after the timed window, time N more back-to-back launches (0: skip); "
+                        "reported beside the result, never as the result")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after timing, run one plain device copy of this many MiB (a kernel of "
                         "known traffic, to scale hardware byte counters against)")
@@ -143,6 +146,26 @@ def main(argv=None) -> int:
         print("bench.py: non-finite output", file=sys.stderr)
         return 1
 
+    # The engine clock is power-managed: after the idle pause the first
+    # launches run fast, the clock then dips below its settled value and
+    # recovers over ~20 ms.  A longer back-to-back window shows where it
+    # settles; the result above keeps the 30-launch window of the protocol.
+    throttle = None
+    if args.throttle_check > 0:
+        s2 = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        s2.record(stream)
+        for _ in range(args.throttle_check):
+            binding.gemm_nt_f16_ex(ta, tb, out=out, variant=vid)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        ms2 = s2.elapsed_time(e2) / args.throttle_check
+        throttle = {"launches": args.throttle_check, "ms_per_launch": ms2,
+                    "tflops": w.flops / (ms2 * 1e-3) / 1e12,
+                    "window": "back-to-back launches right after the timed ones"}
+        log("bench: next %d launches: %.4f ms per launch (%.1f TFLOP/s)"
+            % (args.throttle_check, ms2, throttle["tflops"]))
+
     if args.copy_calibration > 0:
         n = args.copy_calibration * 2 ** 20 // 2
         src = torch.ones(n, dtype=torch.float16, device=dev)
@@ -181,6 +204,8 @@ def main(argv=None) -> int:
                    "output": "f16", "kernel": vname, "pct_of_peak": 100 * tflops / PEAK_TFLOPS},
         "roofline": roof,
     }
+    if throttle is not None:
+        rec["throttle_check"] = throttle
     if args.cpu_rows > 0:
         rows = min(args.cpu_rows, w.M)
         log("bench: timing the CPU oracle on %d rows ..." % rows)
