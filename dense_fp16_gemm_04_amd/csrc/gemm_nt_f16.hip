@@ -39,15 +39,22 @@
 // every fragment read conflict-free except 64-byte rows under 16x16x32
 // MFMAs, which get their own XOR term (swz).
 //
-// Matrix-core step: v_mfma_f32_32x32x16_f16.  Operand lane l holds 8
-// consecutive-k fp16 values of row (l % 32), k offset 8 * (l / 32); the same
-// k mapping is used for both operands, so the contraction is over matching k
-// whatever order the hardware multiplies them in.  The B fragment is passed
-// as the first operand and the A fragment as the second, which makes the
-// 32 x 32 result C^T: lane l then holds row m = l % 32 of C and, in
-// accumulator register r, column n = 8 * (r / 4) + 4 * (l / 32) + r % 4, i.e.
-// four consecutive columns per group of four registers, stored as one 8-byte
-// write.
+// Matrix-core step: v_mfma_f32_16x16x32_f16 (the kernels the library
+// selects) or v_mfma_f32_32x32x16_f16 (ablations).  Operand lane l holds 8
+// consecutive-k fp16 values of row (l % MI), k offset 8 * (l / MI), MI = 16
+// or 32; the same k mapping is used for both operands, so the contraction is
+// over matching k whatever order the hardware multiplies them in.  The B
+// fragment is passed as the first operand and the A fragment as the second,
+// which makes the result block C^T: lane l then holds row m = l % MI of C
+// and, in accumulator register r, column n = 8 * (r / 4) + 4 * (l / MI) +
+// r % 4 (16x16: the four columns 4 * (l / 16) .. +3), i.e. four consecutive
+// columns per group of four registers, stored as one 8-byte piece.
+//
+// Kernels: gemm_nt_f16_mfma (compiler-scheduled, any TileShape),
+// gemm_nt_f16_ordered (four waves, K loop in a fixed hand-placed order; the
+// default for large shapes), gemm_nt_f16_stream / _asm / _asm_split
+// (persistent and inline-assembly ablations), gemm_nt_f16_simple (one output
+// per thread, for K % 8 != 0 and unaligned operands).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -249,6 +256,24 @@ __device__ __forceinline__ void mfma16_agpr(float4_t& acc, const half8_t& b, con
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a) : "memory");
 }
 
+// Store mode of C, passed to the kernels as `c_vec`: bits 0-1 say which
+// stores the rows allow (2: aligned 16-byte, 1: aligned 8-byte, 0: single
+// elements); kStoreNt asks for nontemporal stores.  The host sets it when
+// the grid has more tiles than the chip has CUs: then later waves of tiles
+// still read operand panels through L2, and C written past L2 leaves them
+// there (8192^3: 2% faster).  With a single wave of tiles the plain stores
+// are faster (4096^3: 5%).
+constexpr int kStoreNt = 4;
+
+template <class V>
+__device__ __forceinline__ void store_c(V v, V* p, bool nt)
+{
+    if (nt)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
 // Epilogue: fp32 -> fp16 (round to nearest even) and store.  In each MFMA
 // block lane l holds row cm (its row in the first block) and, in accumulator
 // registers 4q .. 4q+3, the four consecutive columns cn + 8q .. cn + 8q + 3,
@@ -273,12 +298,12 @@ __device__ __forceinline__ void epilogue(const typename T::acc_t (&acc)[T::FM][T
                 h[1] = (_Float16)acc[i][j][4 * q + 1];
                 h[2] = (_Float16)acc[i][j][4 * q + 2];
                 h[3] = (_Float16)acc[i][j][4 * q + 3];
-                if (c_vec && n + 3 < N) {
-                    *(half4_t*)(crow + n) = h;
+                if ((c_vec & 3) && n + 3 < N) {
+                    store_c(h, (half4_t*)(crow + n), c_vec & kStoreNt);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (n + e < N) crow[n + e] = h[e];
+                        if (n + e < N) store_c(h[e], crow + n + e, c_vec & kStoreNt);
                 }
             }
         }
@@ -298,7 +323,7 @@ __device__ __forceinline__ void epilogue(const typename T::acc_t (&acc)[T::FM][T
 template <class T>
 __device__ __forceinline__ void epilogue_lds(const typename T::acc_t (&acc)[T::FM][T::FN], _Float16* __restrict__ C,
                                              int M, int N, int m0, int n0, int wm, int wn, int lane, int wave,
-                                             unsigned char* smem)
+                                             unsigned char* smem, bool nt)
 {
     constexpr int PITCH = T::BN * 2;              // bytes per tile row
     constexpr int CH = T::BN / 8;                  // 16-byte chunks per row
@@ -333,15 +358,16 @@ __device__ __forceinline__ void epilogue_lds(const typename T::acc_t (&acc)[T::F
         const int r = (wave * ITERS + it) * RPL + lr;
         const half8_t v = *(const half8_t*)(smem + r * PITCH + ((lc ^ (r & SW)) << 4));
         const int m = m0 + r, n = n0 + lc * 8;
-        if (m < M && n < N) *(half8_t*)(C + (size_t)m * N + n) = v;
+        if (m < M && n < N) store_c(v, (half8_t*)(C + (size_t)m * N + n), nt);
     }
 }
 
 // Main MFMA kernel.  Requirements checked on the host: A and B 16-byte
-// aligned, K % 8 == 0, K < 2^22, M, N < 2^31.  `c_vec` says which stores C
-// rows allow: 2 for aligned 16-byte stores (N % 8 == 0, C 16-byte aligned;
-// the tile then leaves through LDS), 1 for aligned 8-byte stores (N % 4 ==
-// 0, C 8-byte aligned), 0 for single elements.
+// aligned, K % 8 == 0, K < 2^22, M, N < 2^31.  `c_vec` is the store mode:
+// bits 0-1 say which stores C rows allow, 2 for aligned 16-byte stores (N %
+// 8 == 0, C 16-byte aligned; the tile then leaves through LDS), 1 for
+// aligned 8-byte stores (N % 4 == 0, C 8-byte aligned), 0 for single
+// elements; kStoreNt selects nontemporal stores.
 template <class T>
 __global__ void __launch_bounds__(T::THREADS, T::OCC)
 gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
@@ -599,9 +625,9 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 
     // Small tiles (64 x 64) keep the direct stores: their epilogue is short
     // and the two extra barriers cost more than the wider stores save.
-    if (T::BM * T::BN >= 128 * 128 && c_vec == 2) {
+    if (T::BM * T::BN >= 128 * 128 && (c_vec & 3) == 2) {
         __syncthreads();  // every wave is done with the ring
-        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem);
+        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem, c_vec & kStoreNt);
     } else {
         epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
     }
@@ -765,9 +791,9 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     }
 
-    if (c_vec == 2) {
+    if ((c_vec & 3) == 2) {
         __syncthreads();  // every wave is done with the ring
-        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem);
+        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem, c_vec & kStoreNt);
     } else {
         epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
     }
@@ -1499,13 +1525,24 @@ struct Variant {
     int (*launch)(const void*, const void*, void*, int64_t, int64_t, int64_t, int, hipStream_t);
 };
 
+int num_cus(int device);
+
+// Store mode of C (see kStoreNt) for a grid of `tiles` tiles.
+int c_store_mode(int64_t N, const void* C, int64_t tiles)
+{
+    const int vec = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 2 : ((N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    return vec | (tiles > num_cus(dev) ? kStoreNt : 0);
+}
+
 template <class T>
 int launch_mfma(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int group_m,
                 hipStream_t stream)
 {
     const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
-    const int c_vec = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 2 : ((N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0);
+    const int c_vec = c_store_mode(N, C, tiles_m * tiles_n);
     hipLaunchKernelGGL((gemm_nt_f16_mfma<T>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS),
                        0, stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M,
                        (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
@@ -1518,7 +1555,7 @@ int launch_ordered(const void* A, const void* B, void* C, int64_t M, int64_t N, 
 {
     const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
-    const int c_vec = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 2 : ((N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0);
+    const int c_vec = c_store_mode(N, C, tiles_m * tiles_n);
     hipLaunchKernelGGL((gemm_nt_f16_ordered<T, RS, LS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0,
                        stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N, (int)K,
                        (int)tiles_m, (int)tiles_n, group_m, c_vec);
