@@ -664,9 +664,8 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
                     _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
                     int group_m, int c_vec)
 {
-    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && T::LOADERS == T::WAVES && T::OCC == 1 &&
-                      T::WAVES == 4,
-                  "16x16x32 MFMAs, two sub-steps per step, four waves, every wave loads");
+    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && (T::WAVES == 4 || T::WAVES == 8),
+                  "16x16x32 MFMAs, two sub-steps per step, one or two waves per SIMD");
     constexpr int S = T::STAGES;
     constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
     constexpr int R = T::FM + T::FN;  // fragment reads per sub-step
@@ -686,16 +685,18 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * row_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * row_bytes);
 
-    // Load l < A_LOADS fills KiB (wave * A_LOADS + l) of the stage's A tile,
-    // the others KiB (wave * B_LOADS + l - A_LOADS) of its B tile; lane
-    // placement and swizzle as in gemm_nt_f16_mfma.
+    // Waves 0 .. LOADERS-1 load.  Load l < A_LOADS of loading wave lw fills
+    // KiB (lw * A_LOADS + l) of the stage's A tile, the others KiB (lw *
+    // B_LOADS + l - A_LOADS) of its B tile; lane placement and swizzle as in
+    // gemm_nt_f16_mfma.
+    const int lw = wave < T::LOADERS ? wave : 0;
     const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
     uint32_t voff[T::LOADS];
     int kc[T::LOADS];  // first k of the fetched chunk
 #pragma unroll
     for (int l = 0; l < T::LOADS; ++l) {
         const bool is_a = l < T::A_LOADS;
-        const int row = (wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? l : l - T::A_LOADS)) * T::ROWS_PER_LOAD +
+        const int row = (lw * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? l : l - T::A_LOADS)) * T::ROWS_PER_LOAD +
                         ld_r;
         const int c = swz<T>(row, ld_p);
         voff[l] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
@@ -709,11 +710,11 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
         const uint32_t soff = (uint32_t)k0 * 2u;
         unsigned char* st = smem + stage * T::STAGE_BYTES;
         if (l < T::A_LOADS)  // (a buffer resource cannot be the result of ?:)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st + (wave * T::A_LOADS + l) * 1024), 16, v,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st + (lw * T::A_LOADS + l) * 1024), 16, v,
                                                      soff, 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void_t*)(st + T::A_BYTES + (wave * T::B_LOADS + l - T::A_LOADS) * 1024), 16, v, soff, 0, 0);
+                rb, (lds_void_t*)(st + T::A_BYTES + (lw * T::B_LOADS + l - T::A_LOADS) * 1024), 16, v, soff, 0, 0);
     };
 
     const int fr_row = lane % T::MI;
@@ -760,13 +761,17 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
     };
 
     const int nk = (K + T::BK - 1) / T::BK;
-    if (nk > 0) {
+    // The K loop, compiled once for loading waves and, when only some waves
+    // load, once for the others.
+    auto run = [&](auto ldtag) __attribute__((always_inline)) {
+        constexpr bool LD = decltype(ldtag)::value;
         // every stage is free at the start: fill them all, then wait for
         // step 0 only
 #pragma unroll
         for (int s = 0; s < S; ++s)
 #pragma unroll
-            for (int l = 0; l < T::LOADS; ++l) issue_load(s, s, l, Flag<true>{});
+            for (int l = 0; l < T::LOADS; ++l)
+                if constexpr (LD) issue_load(s, s, l, Flag<true>{});
         lds_barrier<T::LOADS * (S - 1)>();
 #pragma unroll
         for (int idx = 0; idx < R; ++idx) read_one(0, smem, idx);
@@ -776,13 +781,19 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
             substep(0, smem + cur * T::STAGE_BYTES, Flag<false>{}, 0, 0, masked);
             lds_barrier<T::LOADS * (S - 2)>();
             // steps past the end of K load zeros into stages never read
-            substep(1, smem + nxt * T::STAGE_BYTES, Flag<true>{}, cur, ks + S, masked);
+            substep(1, smem + nxt * T::STAGE_BYTES, Flag<LD>{}, cur, ks + S, masked);
             cur = nxt;
         };
         const int nfull = K / T::BK;  // steps that lie wholly inside K
         int ks = 0;
         for (; ks < nk && ks + S < nfull; ++ks) step(ks, Flag<false>{});
         for (; ks < nk; ++ks) step(ks, Flag<true>{});
+    };
+    if (nk > 0) {
+        if (T::LOADERS == T::WAVES || wave < T::LOADERS)
+            run(Flag<true>{});
+        else
+            run(Flag<false>{});
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         // The compiler cannot see that the asm statements are MFMAs: give
         // the last ones time to write their accumulators before they are
@@ -1656,6 +1667,8 @@ constexpr Variant kVariants[] = {
     {"mfma16_256x256x64_w8_s2_l4", 256, 256, 8, launch_mfma<T256_k64_s2_w8_l4_mi16>},
     {"mfma16_256x256x64_w4_s2_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w4_mi16, 4, 4>},
     {"mfma16_256x128x64_w4_s3_ordered", 256, 128, 8, launch_ordered<T256x128_k64_s3_w4_mi16, 2, 2>},
+    {"mfma16_256x256x64_w8_s2_l4_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w8_l4_mi16, 2, 2>},
+    {"mfma16_256x128x64_w8_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4_mi16>},
     {"mfma16_256x128x64_w8_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w8_mi16>},
     {"mfma16_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4_mi16>},
@@ -1711,17 +1724,14 @@ constexpr int variant_index(const char* name)
     return -1;
 }
 
-// Shape -> variant.  Five kernels (four tile sizes) compete; each is priced
+// Shape -> variant.  Four kernels (four tile sizes) compete; each is priced
 // as
 //   ceil(tiles / 256 CUs) x (tile flops / per-CU rate + fixed cost),
 // i.e. whole waves of tiles over the chip (one workgroup per CU), with the
 // per-CU rate each kernel sustains on a full chip (measured on MI355X at
 // 4096^3 .. 8192^3, fp16 random data) and a fixed per-wave cost for launch,
 // pipeline fill and epilogue.  Small problems then take small tiles (more
-// CUs busy), large ones a 256 x 256 kernel (most reuse per byte loaded).
-// Of the two 256 x 256 kernels the 4-wave hand-ordered one has the higher
-// rate and the 8-wave one the shorter fill and epilogue, which wins when K
-// is short (4096 x 4096 x 1024: 34.3 against 35.6 us).
+// CUs busy), large ones the 256 x 256 kernel (most reuse per byte loaded).
 struct Candidate {
     int variant;
     int bm, bn;
@@ -1731,15 +1741,13 @@ struct Candidate {
 
 constexpr int kCUs = 256;
 constexpr Candidate kCandidates[] = {
-    {variant_index("mfma16_256x256x64_w4_s2_ordered"), 256, 256, 1290.0, 5.5},
-    {variant_index("mfma16_256x256x64_w8_s2_l4"), 256, 256, 1230.0, 3.0},
-    {variant_index("mfma16_256x128x64_w4_s3_ordered"), 256, 128, 1100.0, 3.0},
+    {variant_index("mfma16_256x256x64_w8_s2_l4_ordered"), 256, 256, 1290.0, 3.0},
+    {variant_index("mfma16_256x128x64_w8_s3_l4_ordered"), 256, 128, 1170.0, 3.0},
     {variant_index("mfma16_128x128x64_w8_s3"), 128, 128, 900.0, 3.0},
     {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 650.0, 3.0},
 };
-static_assert(variant_index("mfma16_256x256x64_w4_s2_ordered") >= 0 &&
-                  variant_index("mfma16_256x256x64_w8_s2_l4") >= 0 &&
-                  variant_index("mfma16_256x128x64_w4_s3_ordered") >= 0 &&
+static_assert(variant_index("mfma16_256x256x64_w8_s2_l4_ordered") >= 0 &&
+                  variant_index("mfma16_256x128x64_w8_s3_l4_ordered") >= 0 &&
                   variant_index("mfma16_128x128x64_w8_s3") >= 0 && variant_index("mfma16_64x64x64_w4_s3") >= 0,
               "selected variants are in the table");
 

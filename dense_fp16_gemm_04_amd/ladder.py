@@ -54,11 +54,13 @@ RUNGS = {
     "mfma16_256x256x64_w8_s2": "16x16x32 MFMAs, 8 waves (2 per SIMD, 128x64 each)",
     "mfma16_256x256x32_w8_s4": "16x16x32 MFMAs, 8 waves, BK 32 with a 4-stage ring",
     "mfma16_256x256x64_w8x_s2": "16x16x32 MFMAs, 8 waves laid out 4x2 (64x128 each)",
-    "mfma16_256x256x64_w8_s2_l4": "16x16x32 MFMAs, 8 waves, 4 of them loading (default when K is short)",
-    "mfma16_256x256x64_w4_s2_ordered": "4 waves again, every read and load placed by hand, one per 4 MFMAs: the default",
+    "mfma16_256x256x64_w8_s2_l4": "16x16x32 MFMAs, 8 waves, 4 of them loading",
+    "mfma16_256x256x64_w4_s2_ordered": "4 waves again, every read and load placed by hand, one per 4 MFMAs",
+    "mfma16_256x256x64_w8_s2_l4_ordered": "8 waves, 4 loading, every read and load placed by hand: the default",
     "mfma16_256x128x64_w4_s3": "16x16x32 MFMAs, 256x128 tile, 4 waves",
     "mfma16_256x128x64_w8_s3": "16x16x32 MFMAs, 256x128 tile, 8 waves",
-    "mfma16_256x128x64_w4_s3_ordered": "256x128 tile, 4 waves, issue order fixed by hand (default for one GPU's share)",
+    "mfma16_256x128x64_w4_s3_ordered": "256x128 tile, 4 waves, issue order fixed by hand",
+    "mfma16_256x128x64_w8_s3_l4_ordered": "256x128 tile, 8 waves, 4 loading, issue order fixed by hand (default for one GPU's share)",
     "mfma16_128x128x64_w4_s3": "16x16x32 MFMAs, 128x128 tile, 4 waves",
     "mfma16_128x128x64_w8_s3": "16x16x32 MFMAs, 128x128 tile, 8 waves (default for mid sizes)",
     "mfma16_64x64x64_w4_s3": "16x16x32 MFMAs, 64x64 tile (default for small sizes)",

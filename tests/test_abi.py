@@ -61,17 +61,17 @@ def test_selection(lib):
         assert 0 <= v < n
         assert binding.gemm_nt_f16_config_name(w.M, w.N, w.K).startswith("mfma")
     name = binding.gemm_nt_f16_config_name
-    assert name(8192, 8192, 8192) == "mfma16_256x256x64_w4_s2_ordered"
-    assert name(4096, 4096, 4096) == "mfma16_256x256x64_w4_s2_ordered"
-    assert name(5000, 3000, 6000) == "mfma16_256x256x64_w4_s2_ordered"
-    # short K: the 8-wave kernel's shorter fill and epilogue win
-    assert name(4096, 4096, 1024) == "mfma16_256x256x64_w8_s2_l4"
+    assert name(8192, 8192, 8192) == "mfma16_256x256x64_w8_s2_l4_ordered"
+    assert name(4096, 4096, 4096) == "mfma16_256x256x64_w8_s2_l4_ordered"
+    assert name(5000, 3000, 6000) == "mfma16_256x256x64_w8_s2_l4_ordered"
+    assert name(4096, 4096, 1024) == "mfma16_256x256x64_w8_s2_l4_ordered"
+    assert name(2048, 2048, 8192) == "mfma16_128x128x64_w8_s3"
     assert name(2048, 2048, 2048) == "mfma16_128x128x64_w8_s3"
     assert name(1024, 1024, 1024) == "mfma16_64x64x64_w4_s3"
     assert name(256, 256, 256) == "mfma16_64x64x64_w4_s3"
     # one GPU's share of an 8192^3 product split eight ways along M or N
-    assert name(1024, 8192, 8192) == "mfma16_256x128x64_w4_s3_ordered"
-    assert name(8192, 1024, 8192) == "mfma16_256x128x64_w4_s3_ordered"
+    assert name(1024, 8192, 8192) == "mfma16_256x128x64_w8_s3_l4_ordered"
+    assert name(8192, 1024, 8192) == "mfma16_256x128x64_w8_s3_l4_ordered"
     # K not a multiple of 8 cannot use the MFMA kernels
     assert binding.gemm_nt_f16_config_name(64, 64, 7).startswith("simple")
     assert lib.gemm_nt_f16_select(-1, 4, 4) == -1
