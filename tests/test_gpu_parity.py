@@ -248,10 +248,13 @@ def test_edge_shapes_every_variant():
             assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), (M, N, K, name)
 
 
-@pytest.mark.parametrize("M,N,K", [(5000, 6000, 72), (8192, 8192, 128), (2304, 9000, 8)])
+@pytest.mark.parametrize("M,N,K", [(5000, 6000, 72), (8192, 8192, 128), (2304, 9000, 8),
+                                   (4100, 4100, 72), (4097, 4097, 16)])
 def test_many_tiles_per_workgroup_every_variant(M, N, K):
     """Shapes with more tiles than compute units, so the persistent kernels
-    stream several tiles (and their K tails) through one workgroup."""
+    stream several tiles (and their K tails) through one workgroup and the
+    others store C with the nontemporal hint; N = 4100 and 4097 take that
+    hint with 8-byte and single-element stores."""
     a, b = workloads.small_integers(M, N, K, seed=M + N + K)
     _, c16 = oracle.gemm_nt(a, b)
     for name, vid in variant_ids().items():
