@@ -633,24 +633,29 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     }
 }
 
-// One wave per SIMD, every instruction of the K loop in a fixed order.
+// Every instruction of the K loop in a fixed order.
 //
-// Four waves each own a quarter of the tile (for 256 x 256: 128 x 128, i.e.
-// 8 x 8 blocks of 16 x 16 and 256 accumulator floats per lane, every AGPR).
-// With one wave per SIMD nothing else issues while this wave waits, so
-// stalls cannot be covered by a partner wave as in the 8-wave kernel;
-// instead nothing is bunched.  A BK = 64 step is two sub-steps of 32 k
-// (FM x FN MFMAs each):
+// Four or eight waves (one or two per SIMD) each own a sub-tile of C (for
+// 256 x 256 with 8 waves: 128 x 64, i.e. 8 x 4 blocks of 16 x 16 and 128
+// accumulator floats per lane in AGPRs); waves 0 .. LOADERS-1 issue the
+// global->LDS loads.  Nothing is bunched, so no wave stalls for long.  A
+// BK = 64 step is two sub-steps of 32 k (FM x FN MFMAs each):
 //   sub-step 0: its MFMAs, and after every RS-th of them one fragment read
 //               of sub-step 1;
-//   barrier:    this wave's loads of step ks + 1 have landed (vmcnt: only
-//               the loads of the STAGES - 2 later steps may still be in
-//               flight), its reads of sub-step 1 have returned; every wave
-//               is done with this step's stage;
+//   barrier:    this wave's loads of step ks + 1 have landed (vmcnt), its
+//               reads of sub-step 1 have returned; every wave is done with
+//               this step's operand tiles;
 //   sub-step 1: its MFMAs, with one fragment read of the next step's
-//               sub-step 0 after every RS-th, and one of this wave's
-//               global->LDS loads of step ks + STAGES (into this step's
-//               stage) after every LS-th, starting half-way into the first.
+//               sub-step 0 after every RS-th, and this wave's loads after
+//               every LS-th, starting half-way into the first.
+// LDS is either a ring of STAGES stages (A and B tiles of one step each;
+// sub-step 1 loads step ks + STAGES into the stage step ks leaves) or, with
+// SLOTS5, five slots of one operand tile each (A_j in slot 2j mod 5, B_j in
+// slot 2j + 1 mod 5, 160 KiB for 256 x 256): then sub-step 0 loads A_{j+2}
+// into the slot B_{j-1} left and sub-step 1 loads B_{j+2} into the slot A_j
+// leaves, so the loads are spread over the whole step and the A tiles get
+// half a step more time to land (8192^3: +2%, 5000 x 3000 x 6000: +8%
+// over the 2-stage ring).
 // The MFMAs are asm statements (mfma16_agpr), which keeps the accumulators
 // in place: compiled from the builtin, a kernel whose accumulators fill all
 // 256 AGPRs moves them between AGPRs and VGPRs inside the loop (1.3 copies
@@ -658,7 +663,7 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 // (A block 0, B blocks 0 .. FN-1, A blocks 1 .. FM-1), so the compiler's
 // lgkmcnt waits before each MFMA only cover reads issued long before.  Loads
 // of steps that lie wholly inside K skip the per-lane K check.
-template <class T, int RS, int LS>
+template <class T, int RS, int LS, bool SLOTS5 = false>
 __global__ void __launch_bounds__(T::THREADS, 1)
 gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                     _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
@@ -669,8 +674,12 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
     constexpr int S = T::STAGES;
     constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
     constexpr int R = T::FM + T::FN;  // fragment reads per sub-step
-    static_assert(RS * (R - 1) < G && LS * (T::LOADS - 1) + LS / 2 < G, "reads and loads fit in a sub-step");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
+    constexpr int LOADS_SUB = SLOTS5 ? T::A_LOADS : T::LOADS;  // loads per loading sub-step
+    static_assert(RS * (R - 1) < G && LS * (LOADS_SUB - 1) + LS / 2 < G, "reads and loads fit in a sub-step");
+    constexpr int SLOT = T::A_BYTES;  // SLOTS5: one operand tile of one step
+    static_assert(!SLOTS5 || (T::A_BYTES == T::B_BYTES && 5 * SLOT <= 160 * 1024 && 5 * SLOT >= T::LDS_BYTES),
+                  "five equal slots, at least as much LDS as the ring");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[SLOTS5 ? 5 * SLOT : T::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -702,19 +711,22 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
         voff[l] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
         kc[l] = c * 8;
     }
-    // MASKED: the step may reach past K (chunks at or past K read as zero)
-    auto issue_load = [&](int stage, int kstep, int l, auto masked) __attribute__((always_inline)) {
+    // Load l of step kstep into stage `where` (SLOTS5: into slot `where`,
+    // which holds the load's operand tile).  MASKED: the step may reach
+    // past K (chunks at or past K read as zero).
+    auto issue_load = [&](int where, int kstep, int l, auto masked) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked)::value;
         const int k0 = kstep * T::BK;
         const uint32_t v = (!MASKED || kc[l] < K - k0) ? voff[l] : kOob;
         const uint32_t soff = (uint32_t)k0 * 2u;
-        unsigned char* st = smem + stage * T::STAGE_BYTES;
+        unsigned char* a_tile = smem + where * (SLOTS5 ? SLOT : T::STAGE_BYTES);
+        unsigned char* b_tile = SLOTS5 ? a_tile : a_tile + T::A_BYTES;
         if (l < T::A_LOADS)  // (a buffer resource cannot be the result of ?:)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st + (lw * T::A_LOADS + l) * 1024), 16, v,
-                                                     soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(a_tile + (lw * T::A_LOADS + l) * 1024), 16,
+                                                     v, soff, 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void_t*)(st + T::A_BYTES + (lw * T::B_LOADS + l - T::A_LOADS) * 1024), 16, v, soff, 0, 0);
+                rb, (lds_void_t*)(b_tile + (lw * T::B_LOADS + l - T::A_LOADS) * 1024), 16, v, soff, 0, 0);
     };
 
     const int fr_row = lane % T::MI;
@@ -735,9 +747,11 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
 #pragma unroll
             for (int r = 0; r < T::ACC; ++r) acc[i][j][r] = 0.0f;
 
-    auto read_one = [&](int set, const unsigned char* base, int idx) __attribute__((always_inline)) {
-        const unsigned char* pa = base + a_row0 * T::ROW_BYTES + fr_pos[set];
-        const unsigned char* pb = base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[set];
+    // fragment read `idx` of sub-step `set` from A tile at abase, B tile at bbase
+    auto read_one = [&](int set, const unsigned char* abase, const unsigned char* bbase, int idx)
+                        __attribute__((always_inline)) {
+        const unsigned char* pa = abase + a_row0 * T::ROW_BYTES + fr_pos[set];
+        const unsigned char* pb = bbase + b_row0 * T::ROW_BYTES + fr_pos[set];
         if (idx == 0)
             fa[set][0] = *(const half8_t*)pa;
         else if (idx <= T::FN)
@@ -746,17 +760,17 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
             fa[set][idx - T::FN] = *(const half8_t*)(pa + (idx - T::FN) * T::MI * T::ROW_BYTES);
     };
     // MFMAs of sub-step `cs` (block row i = t / FN, column j = t % FN), with
-    // the reads of sub-step 1 - cs from `rbase` and, if LD, the loads of
-    // step `lstep` into `lstage` interleaved.
-    auto substep = [&](int cs, const unsigned char* rbase, auto ld, int lstage, int lstep, auto masked)
-                       __attribute__((always_inline)) {
+    // the reads of sub-step 1 - cs from (ra_base, rb_base) and, if LD, loads
+    // [l0, l0 + LOADS_SUB) of step `lstep` into `where` interleaved.
+    auto substep = [&](int cs, const unsigned char* ra_base, const unsigned char* rb_base, auto ld, int where,
+                       int lstep, int l0, auto masked) __attribute__((always_inline)) {
         constexpr bool LD = decltype(ld)::value;
 #pragma unroll
         for (int t = 0; t < G; ++t) {
             mfma16_agpr(acc[t / T::FN][t % T::FN], fb[cs][t % T::FN], fa[cs][t / T::FN]);
-            if (t % RS == 0 && t / RS < R) read_one(1 - cs, rbase, t / RS);
+            if (t % RS == 0 && t / RS < R) read_one(1 - cs, ra_base, rb_base, t / RS);
             if constexpr (LD)
-                if (t % LS == LS / 2 && t / LS < T::LOADS) issue_load(lstage, lstep, t / LS, masked);
+                if (t % LS == LS / 2 && t / LS < LOADS_SUB) issue_load(where, lstep, l0 + t / LS, masked);
         }
     };
 
@@ -765,29 +779,59 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
     // load, once for the others.
     auto run = [&](auto ldtag) __attribute__((always_inline)) {
         constexpr bool LD = decltype(ldtag)::value;
-        // every stage is free at the start: fill them all, then wait for
-        // step 0 only
-#pragma unroll
-        for (int s = 0; s < S; ++s)
-#pragma unroll
-            for (int l = 0; l < T::LOADS; ++l)
-                if constexpr (LD) issue_load(s, s, l, Flag<true>{});
-        lds_barrier<T::LOADS * (S - 1)>();
-#pragma unroll
-        for (int idx = 0; idx < R; ++idx) read_one(0, smem, idx);
-        int cur = 0;  // stage of step ks
-        auto step = [&](int ks, auto masked) __attribute__((always_inline)) {
-            const int nxt = cur + 1 == S ? 0 : cur + 1;
-            substep(0, smem + cur * T::STAGE_BYTES, Flag<false>{}, 0, 0, masked);
-            lds_barrier<T::LOADS * (S - 2)>();
-            // steps past the end of K load zeros into stages never read
-            substep(1, smem + nxt * T::STAGE_BYTES, Flag<LD>{}, cur, ks + S, masked);
-            cur = nxt;
-        };
         const int nfull = K / T::BK;  // steps that lie wholly inside K
-        int ks = 0;
-        for (; ks < nk && ks + S < nfull; ++ks) step(ks, Flag<false>{});
-        for (; ks < nk; ++ks) step(ks, Flag<true>{});
+        if constexpr (SLOTS5) {
+            // steps 0 and 1 into slots 0 .. 3, then wait for step 0 only
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int l = 0; l < T::LOADS; ++l)
+                    if constexpr (LD) issue_load(l < T::A_LOADS ? 2 * s : 2 * s + 1, s, l, Flag<true>{});
+            lds_barrier<T::LOADS>();
+#pragma unroll
+            for (int idx = 0; idx < R; ++idx) read_one(0, smem, smem + SLOT, idx);
+            int sa = 0;  // slot of A_j; B_j, A_{j+1}, B_{j+1}, A_{j+2} follow
+            auto slot = [&](int i) __attribute__((always_inline)) {
+                return smem + (sa + i >= 5 ? sa + i - 5 : sa + i) * SLOT;
+            };
+            auto step = [&](int ks, auto masked) __attribute__((always_inline)) {
+                const int a2 = sa + 4 >= 5 ? sa - 1 : sa + 4;
+                substep(0, slot(0), slot(1), Flag<LD>{}, a2, ks + 2, 0, masked);
+                // A_{j+1} and B_{j+1} have landed; only A_{j+2} may be in flight
+                lds_barrier<T::A_LOADS>();
+                // steps past the end of K load zeros into slots never read
+                substep(1, slot(2), slot(3), Flag<LD>{}, sa, ks + 2, T::A_LOADS, masked);
+                sa = sa + 2 >= 5 ? sa - 3 : sa + 2;
+            };
+            int ks = 0;
+            for (; ks < nk && ks + 2 < nfull; ++ks) step(ks, Flag<false>{});
+            for (; ks < nk; ++ks) step(ks, Flag<true>{});
+        } else {
+            // every stage is free at the start: fill them all, then wait for
+            // step 0 only
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int l = 0; l < T::LOADS; ++l)
+                    if constexpr (LD) issue_load(s, s, l, Flag<true>{});
+            lds_barrier<T::LOADS * (S - 1)>();
+#pragma unroll
+            for (int idx = 0; idx < R; ++idx) read_one(0, smem, smem + T::A_BYTES, idx);
+            int cur = 0;  // stage of step ks
+            auto step = [&](int ks, auto masked) __attribute__((always_inline)) {
+                const int nxt = cur + 1 == S ? 0 : cur + 1;
+                unsigned char* base = smem + cur * T::STAGE_BYTES;
+                unsigned char* next = smem + nxt * T::STAGE_BYTES;
+                substep(0, base, base + T::A_BYTES, Flag<false>{}, 0, 0, 0, masked);
+                lds_barrier<T::LOADS * (S - 2)>();
+                // steps past the end of K load zeros into stages never read
+                substep(1, next, next + T::A_BYTES, Flag<LD>{}, cur, ks + S, 0, masked);
+                cur = nxt;
+            };
+            int ks = 0;
+            for (; ks < nk && ks + S < nfull; ++ks) step(ks, Flag<false>{});
+            for (; ks < nk; ++ks) step(ks, Flag<true>{});
+        }
     };
     if (nk > 0) {
         if (T::LOADERS == T::WAVES || wave < T::LOADERS)
@@ -1560,14 +1604,14 @@ int launch_mfma(const void* A, const void* B, void* C, int64_t M, int64_t N, int
     return (int)hipGetLastError();
 }
 
-template <class T, int RS, int LS>
+template <class T, int RS, int LS, bool SLOTS5 = false>
 int launch_ordered(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int group_m,
                    hipStream_t stream)
 {
     const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
     const int c_vec = c_store_mode(N, C, tiles_m * tiles_n);
-    hipLaunchKernelGGL((gemm_nt_f16_ordered<T, RS, LS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_nt_f16_ordered<T, RS, LS, SLOTS5>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0,
                        stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N, (int)K,
                        (int)tiles_m, (int)tiles_n, group_m, c_vec);
     return (int)hipGetLastError();
@@ -1668,6 +1712,7 @@ constexpr Variant kVariants[] = {
     {"mfma16_256x256x64_w4_s2_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w4_mi16, 4, 4>},
     {"mfma16_256x128x64_w4_s3_ordered", 256, 128, 8, launch_ordered<T256x128_k64_s3_w4_mi16, 2, 2>},
     {"mfma16_256x256x64_w8_s2_l4_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w8_l4_mi16, 2, 2>},
+    {"mfma16_256x256x64_w8_r5_l4_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w8_l4_mi16, 2, 2, true>},
     {"mfma16_256x128x64_w8_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4_mi16>},
     {"mfma16_256x128x64_w8_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w8_mi16>},
@@ -1741,12 +1786,12 @@ struct Candidate {
 
 constexpr int kCUs = 256;
 constexpr Candidate kCandidates[] = {
-    {variant_index("mfma16_256x256x64_w8_s2_l4_ordered"), 256, 256, 1290.0, 3.0},
+    {variant_index("mfma16_256x256x64_w8_r5_l4_ordered"), 256, 256, 1300.0, 3.0},
     {variant_index("mfma16_256x128x64_w8_s3_l4_ordered"), 256, 128, 1170.0, 3.0},
     {variant_index("mfma16_128x128x64_w8_s3"), 128, 128, 900.0, 3.0},
     {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 650.0, 3.0},
 };
-static_assert(variant_index("mfma16_256x256x64_w8_s2_l4_ordered") >= 0 &&
+static_assert(variant_index("mfma16_256x256x64_w8_r5_l4_ordered") >= 0 &&
                   variant_index("mfma16_256x128x64_w8_s3_l4_ordered") >= 0 &&
                   variant_index("mfma16_128x128x64_w8_s3") >= 0 && variant_index("mfma16_64x64x64_w4_s3") >= 0,
               "selected variants are in the table");
