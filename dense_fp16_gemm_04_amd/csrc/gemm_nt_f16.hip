@@ -51,10 +51,12 @@
 // columns per group of four registers, stored as one 8-byte piece.
 //
 // Kernels: gemm_nt_f16_mfma (compiler-scheduled, any TileShape),
-// gemm_nt_f16_ordered (four waves, K loop in a fixed hand-placed order; the
-// default for large shapes), gemm_nt_f16_stream / _asm / _asm_split
-// (persistent and inline-assembly ablations), gemm_nt_f16_simple (one output
-// per thread, for K % 8 != 0 and unaligned operands).
+// gemm_nt_f16_ordered (four or eight waves, K loop in a fixed hand-placed
+// order, one tile per workgroup), gemm_nt_f16_ordered_persist (its
+// persistent 5-slot form: the default for large shapes),
+// gemm_nt_f16_stream / _asm / _asm_split (32x32x16 persistent and
+// inline-assembly ablations), gemm_nt_f16_simple (one output per thread,
+// for K % 8 != 0 and unaligned operands).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -67,6 +69,7 @@ namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
@@ -91,6 +94,8 @@ constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any tile: loads 0
 
 // Buffer resource word 3 for gfx9-family (data format 32, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy operand of a buffer access: the nontemporal (nt) bit.
+constexpr int kPolicyNt = 2;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits 15:14,
 // expcnt[6:4], lgkmcnt[11:8]); the counters not waited on are left at max.
@@ -256,23 +261,8 @@ __device__ __forceinline__ void mfma16_agpr(float4_t& acc, const half8_t& b, con
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a) : "memory");
 }
 
-// Store mode of C, passed to the kernels as `c_vec`: bits 0-1 say which
-// stores the rows allow (2: aligned 16-byte, 1: aligned 8-byte, 0: single
-// elements); kStoreNt asks for nontemporal stores.  The host sets it when
-// the grid has more tiles than the chip has CUs: then later waves of tiles
-// still read operand panels through L2, and C written past L2 leaves them
-// there (8192^3: 2% faster).  With a single wave of tiles the plain stores
-// are faster (4096^3: 5%).
-constexpr int kStoreNt = 4;
-
-template <class V>
-__device__ __forceinline__ void store_c(V v, V* p, bool nt)
-{
-    if (nt)
-        __builtin_nontemporal_store(v, p);
-    else
-        *p = v;
-}
+// Store mode of C, passed to the kernels as `c_vec`: which stores the rows
+// allow (2: aligned 16-byte, 1: aligned 8-byte, 0: single elements).
 
 // Epilogue: fp32 -> fp16 (round to nearest even) and store.  In each MFMA
 // block lane l holds row cm (its row in the first block) and, in accumulator
@@ -299,11 +289,11 @@ __device__ __forceinline__ void epilogue(const typename T::acc_t (&acc)[T::FM][T
                 h[2] = (_Float16)acc[i][j][4 * q + 2];
                 h[3] = (_Float16)acc[i][j][4 * q + 3];
                 if ((c_vec & 3) && n + 3 < N) {
-                    store_c(h, (half4_t*)(crow + n), c_vec & kStoreNt);
+                    *(half4_t*)(crow + n) = h;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (n + e < N) store_c(h[e], crow + n + e, c_vec & kStoreNt);
+                        if (n + e < N) crow[n + e] = h[e];
                 }
             }
         }
@@ -323,7 +313,7 @@ __device__ __forceinline__ void epilogue(const typename T::acc_t (&acc)[T::FM][T
 template <class T>
 __device__ __forceinline__ void epilogue_lds(const typename T::acc_t (&acc)[T::FM][T::FN], _Float16* __restrict__ C,
                                              int M, int N, int m0, int n0, int wm, int wn, int lane, int wave,
-                                             unsigned char* smem, bool nt)
+                                             unsigned char* smem)
 {
     constexpr int PITCH = T::BN * 2;              // bytes per tile row
     constexpr int CH = T::BN / 8;                  // 16-byte chunks per row
@@ -332,7 +322,12 @@ __device__ __forceinline__ void epilogue_lds(const typename T::acc_t (&acc)[T::F
     constexpr int ITERS = T::BM / RPL / T::WAVES;  // reads per wave
     static_assert(T::BM * PITCH <= T::LDS_BYTES, "the C tile fits in the ring");
     static_assert(RPL >= 1 && ITERS * RPL * T::WAVES == T::BM, "rows split evenly over waves");
-    const int fr_row = lane % T::MI, fr_hi = lane / T::MI;
+    // the lane index recomputed and laundered: the offsets derived from it
+    // are computed here, not early and kept (or spilled) through the K loop
+    int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(ln));
+    (void)lane;
+    const int fr_row = ln % T::MI, fr_hi = ln / T::MI;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
         const int r = wm * T::WTM + i * T::MI + fr_row;
@@ -352,13 +347,33 @@ __device__ __forceinline__ void epilogue_lds(const typename T::acc_t (&acc)[T::F
         }
     }
     __syncthreads();
-    const int lr = lane / CH, lc = lane % CH;
+    const int lr = ln / CH, lc = ln % CH;
+    const int n = n0 + lc * 8;
+    if (N <= (1 << 22)) {
+        // Buffer stores with one 32-bit offset per store: rows past M fall
+        // outside the buffer, columns past N get an offset outside it.  C is
+        // never read back, so it goes out with the nontemporal hint (0.5-3%
+        // faster on every shape measured, one wave of tiles or several).
+        // The hint is an immediate of the buffer store; as a pointer store
+        // under a runtime condition it was lost (the compiler merged it with
+        // the plain store of the other branch).
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (size_t)m0 * N, (uint32_t)min(T::BM, M - m0) * (uint32_t)N * 2u);
+        const uint32_t vbase = n < N ? ((uint32_t)lr * (uint32_t)N + (uint32_t)n) * 2u : kOob;
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-        const int r = (wave * ITERS + it) * RPL + lr;
-        const half8_t v = *(const half8_t*)(smem + r * PITCH + ((lc ^ (r & SW)) << 4));
-        const int m = m0 + r, n = n0 + lc * 8;
-        if (m < M && n < N) store_c(v, (half8_t*)(C + (size_t)m * N + n), nt);
+        for (int it = 0; it < ITERS; ++it) {
+            const int r = (wave * ITERS + it) * RPL + lr;
+            const u32x4_t v = *(const u32x4_t*)(smem + r * PITCH + ((lc ^ (r & SW)) << 4));
+            const uint32_t off = vbase + (uint32_t)((wave * ITERS + it) * RPL) * (uint32_t)N * 2u;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, kPolicyNt);
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int r = (wave * ITERS + it) * RPL + lr;
+            const half8_t v = *(const half8_t*)(smem + r * PITCH + ((lc ^ (r & SW)) << 4));
+            const int m = m0 + r;
+            if (m < M && n < N) *(half8_t*)(C + (size_t)m * N + n) = v;
+        }
     }
 }
 
@@ -367,7 +382,7 @@ __device__ __forceinline__ void epilogue_lds(const typename T::acc_t (&acc)[T::F
 // bits 0-1 say which stores C rows allow, 2 for aligned 16-byte stores (N %
 // 8 == 0, C 16-byte aligned; the tile then leaves through LDS), 1 for
 // aligned 8-byte stores (N % 4 == 0, C 8-byte aligned), 0 for single
-// elements; kStoreNt selects nontemporal stores.
+// elements.
 template <class T>
 __global__ void __launch_bounds__(T::THREADS, T::OCC)
 gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
@@ -627,7 +642,7 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     // and the two extra barriers cost more than the wider stores save.
     if (T::BM * T::BN >= 128 * 128 && (c_vec & 3) == 2) {
         __syncthreads();  // every wave is done with the ring
-        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem, c_vec & kStoreNt);
+        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem);
     } else {
         epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
     }
@@ -848,10 +863,314 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
 
     if ((c_vec & 3) == 2) {
         __syncthreads();  // every wave is done with the ring
-        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem, c_vec & kStoreNt);
+        epilogue_lds<T>(acc, C, M, N, m0, n0, wm, wn, lane, wave, smem);
     } else {
         epilogue<T>(acc, C, M, N, m0 + wm * T::WTM + fr_row, n0 + wn * T::WTN + 4 * fr_hi, c_vec);
     }
+}
+
+// Persistent form of the 5-slot kernel above.  One workgroup per compute
+// unit runs tiles b, b + G, b + 2G, ... (G = grid size, in the tile order of
+// tile_coords).  What a tile costs beyond its K loop is the pipeline's fill
+// and drain and the epilogue ("6. Four Consumers, FP16 Accumulation, and a
+// TMA Epilogue", opening paragraph); here the load stream runs on across
+// tiles: the last two steps of a tile load the first two steps of the next,
+// so only the epilogue and one round of fragment reads stand between two
+// tiles.  It stages C through the two slots the last
+// step leaves free, in two rounds of 128 rows (the pages stage a 256 x 256
+// tile through a quarter-sized buffer in turns, section "Serialized
+// Shared-Memory Epilogue").  All waves write their rows; only the four
+// waves that never load read them back and store them.  A loading wave's
+// barrier waits on its vmcnt, which would also wait for any store it had
+// issued; the non-loading waves never wait on theirs, so the stores drain
+// while the next tile computes.  Host side: K > 64 (two steps at least),
+// C rows allow aligned 16-byte stores.
+template <class T, int RS, int LS>
+__global__ void __launch_bounds__(T::THREADS, 1)
+gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
+                            _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+                            int group_m, int c_vec)
+{
+    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && T::WAVES == 8 && T::LOADERS == 4 &&
+                      T::WAVES_M == 2 && T::NG == 1,
+                  "16x16x32 MFMAs, two sub-steps per step, 2 x 4 waves of which 4 load");
+    constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
+    constexpr int R = T::FM + T::FN;  // fragment reads per sub-step
+    constexpr int SLOT = T::A_BYTES;  // one operand tile of one step
+    static_assert(T::A_BYTES == T::B_BYTES && 5 * SLOT <= 160 * 1024, "five equal slots");
+    static_assert(RS * (R - 1) < G && LS * (T::A_LOADS - 1) + LS / 2 < G, "reads and loads fit in a sub-step");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[5 * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+    const int total = tiles_m * tiles_n;
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const int nk = (K + T::BK - 1) / T::BK;
+    const int nfull = K / T::BK;  // steps that lie wholly inside K
+
+    // Load assignment as in gemm_nt_f16_ordered: load l of loading wave lw
+    // fills rows g * ROWS_PER_LOAD .. + ROWS_PER_LOAD - 1 of its operand tile
+    // (g = lw * A_LOADS + l for A, lw * B_LOADS + l - A_LOADS for B).  The
+    // swizzle repeats every two such row groups and g has the parity of l,
+    // so a lane's offset within its group and the chunk it fetches take two
+    // values, by the parity of l (two registers each instead of one per load).
+    static_assert((T::CHUNKS << T::SWZ_SHIFT) == 2 * T::ROWS_PER_LOAD && T::A_LOADS % 2 == 0 &&
+                      T::B_LOADS % 2 == 0,
+                  "the swizzle repeats every two row groups of a load");
+    const int lw = wave < T::LOADERS ? wave : 0;
+    const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
+    uint32_t vpar[2];
+    int kpar[2];  // first k of the fetched chunk
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int c = swz<T>(p * T::ROWS_PER_LOAD + ld_r, ld_p);
+        vpar[p] = (uint32_t)ld_r * row_bytes + (uint32_t)c * 16u;
+        kpar[p] = c * 8;
+    }
+
+    // The tile being loaded (la, lb: its operand buffers, rows past M or N
+    // read as zero) runs up to one tile ahead of the tile being computed.
+    int tile = blockIdx.x;
+    if (tile >= total) return;  // (the host launches at most one workgroup per tile)
+    int tm, tn;
+    tile_coords(tile, tiles_m, tiles_n, group_m, tm, tn);
+    int m0 = tm * T::BM, n0 = tn * T::BN;
+    __amdgpu_buffer_rsrc_t la = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(T::BM, M - m0) * row_bytes);
+    __amdgpu_buffer_rsrc_t lb = make_rsrc(B + (size_t)n0 * K, (uint32_t)min(T::BN, N - n0) * row_bytes);
+
+    // Load l of step kstep of the loading tile into slot `where`.
+    // (rbytes: row_bytes, laundered by the caller so that the 16 offsets
+    // are computed where they are used, not kept in registers)
+    auto issue_load = [&](int where, int kstep, int l, auto masked, uint32_t rbytes) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const int k0 = kstep * T::BK;
+        const int g = l < T::A_LOADS ? lw * T::A_LOADS + l : lw * T::B_LOADS + l - T::A_LOADS;
+        const uint32_t off = (uint32_t)(g * T::ROWS_PER_LOAD) * rbytes + vpar[l & 1];
+        const uint32_t v = (!MASKED || kpar[l & 1] < K - k0) ? off : kOob;
+        const uint32_t soff = (uint32_t)k0 * 2u;
+        unsigned char* dst = smem + where * SLOT + g * 1024;
+        if (l < T::A_LOADS)  // (a buffer resource cannot be the result of ?:)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(la, (lds_void_t*)dst, 16, v, soff, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(lb, (lds_void_t*)dst, 16, v, soff, 0, 0);
+    };
+
+    const int fr_row = lane % T::MI;
+    const int fr_hi = lane / T::MI;
+    const int a_row0 = wm * T::WTM + fr_row;
+    const int b_row0 = wn * T::WTN + fr_row;
+    int fr_pos[T::KK];
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, T::CPS * kk + fr_hi) * 16;
+
+    half8_t fa[2][T::FM], fb[2][T::FN];
+    typename T::acc_t acc[T::FM][T::FN];
+    // Zero the accumulators in place: an MFMA of zero operands with an inline
+    // zero as its C input.  (Plain writes could be moved next to the first
+    // accumulating MFMA, whose asm hides the VALU-to-MFMA hazard from the
+    // compiler; pinning them in AGPRs with asm operands makes the register
+    // allocator spill.)  The zero operand is written by a VALU move, which an
+    // MFMA may read only a few wait states later: the compiler cannot see
+    // that hazard through the asm, so each statement waits first.
+    auto zero_acc = [&]() __attribute__((always_inline)) {
+        const half8_t z = {};
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+                asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_f16 %0, %1, %1, 0"
+                             : "=a"(acc[i][j])
+                             : "v"(z)
+                             : "memory");
+    };
+
+    auto read_one = [&](int set, const unsigned char* abase, const unsigned char* bbase, int idx)
+                        __attribute__((always_inline)) {
+        const unsigned char* pa = abase + a_row0 * T::ROW_BYTES + fr_pos[set];
+        const unsigned char* pb = bbase + b_row0 * T::ROW_BYTES + fr_pos[set];
+        if (idx == 0)
+            fa[set][0] = *(const half8_t*)pa;
+        else if (idx <= T::FN)
+            fb[set][idx - 1] = *(const half8_t*)(pb + (idx - 1) * T::MI * T::ROW_BYTES);
+        else
+            fa[set][idx - T::FN] = *(const half8_t*)(pa + (idx - T::FN) * T::MI * T::ROW_BYTES);
+    };
+    // MFMAs of sub-step cs, with (if RD) the fragment reads of sub-step 1 -
+    // cs and (if LD) loads l0 .. l0 + A_LOADS - 1 of step lstep interleaved.
+    auto substep = [&](int cs, const unsigned char* ra_base, const unsigned char* rb_base, auto ld, int where,
+                       int lstep, int l0, auto masked, auto rd) __attribute__((always_inline)) {
+        constexpr bool LD = decltype(ld)::value, RD = decltype(rd)::value;
+        uint32_t rbytes = row_bytes;
+        asm volatile("" : "+s"(rbytes));
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+            mfma16_agpr(acc[t / T::FN][t % T::FN], fb[cs][t % T::FN], fa[cs][t / T::FN]);
+            if constexpr (RD)
+                if (t % RS == 0 && t / RS < R) read_one(1 - cs, ra_base, rb_base, t / RS);
+            if constexpr (LD)
+                if (t % LS == LS / 2 && t / LS < T::A_LOADS) issue_load(where, lstep, l0 + t / LS, masked, rbytes);
+        }
+    };
+
+    // Epilogue of the tile at (cm0, cn0) through slots s0 and s1: round h
+    // stages rows h * 64 .. h * 64 + 63 of each wave row (wave row wm into
+    // slot s<wm>), then the non-loading waves store them with nontemporal
+    // buffer stores (as in epilogue_lds: one 32-bit offset per store; rows
+    // past M fall outside the buffer and columns past N get an offset outside
+    // it, so neither is written).
+    auto epilogue = [&](unsigned char* s0, unsigned char* s1, int cm0, int cn0, bool storer)
+                        __attribute__((always_inline)) {
+        constexpr int PITCH = T::BN * 2;           // bytes per staged row
+        constexpr int CH = T::BN / 8;              // 16-byte chunks per row
+        constexpr int SW = CH >= 16 ? 15 : CH - 1;
+        constexpr int HALF = T::FM / 2;            // MFMA block rows per round
+        constexpr int SROWS = SLOT / PITCH;        // staged rows per slot
+        constexpr int RPL = 1024 / PITCH;          // rows per wave-wide 1 KiB read
+        constexpr int STORERS = T::WAVES - T::LOADERS;
+        constexpr int ITERS = 2 * SROWS / RPL / STORERS;  // reads per storing wave per round
+        static_assert(HALF * T::MI == SROWS && ITERS * RPL * STORERS == 2 * SROWS && ITERS % 4 == 0 &&
+                          ITERS * RPL * 2 == SROWS,
+                      "a round fills both slots, each storing wave reads half a slot");
+        unsigned char* mine = wm == 0 ? s0 : s1;
+        const int sw = wave - T::LOADERS;
+        // the lane index laundered: offsets derived from it are computed
+        // here rather than kept (or spilled) through the K loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int e_row = ln % T::MI, e_hi = ln / T::MI;
+        const int lr = ln / CH, lc = ln % CH;
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(C + (size_t)cm0 * N, (uint32_t)min(T::BM, M - cm0) * (uint32_t)N * 2u);
+        // storing wave sw reads rows (sw % 2) * SROWS / 2 + RPL * it + lr of
+        // slot sw / 2, i.e. tile row (sw / 2) * WTM + h * SROWS + that; this
+        // lane's byte offset is vbase plus a wave-uniform part
+        const int n = cn0 + lc * 8;
+        const uint32_t vbase = n < N ? ((uint32_t)lr * (uint32_t)N + (uint32_t)n) * 2u : kOob;
+        const unsigned char* rd = (sw < STORERS / 2 ? s0 : s1) + (sw % 2) * (SROWS / 2) * PITCH;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < HALF; ++i) {
+                const int x = i * T::MI + e_row;
+                unsigned char* lrow = mine + x * PITCH;
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j) {
+                    const int col = wn * T::WTN + j * T::MI + 4 * e_hi;
+                    half4_t v;
+                    v[0] = (_Float16)acc[h * HALF + i][j][0];
+                    v[1] = (_Float16)acc[h * HALF + i][j][1];
+                    v[2] = (_Float16)acc[h * HALF + i][j][2];
+                    v[3] = (_Float16)acc[h * HALF + i][j][3];
+                    *(half4_t*)(lrow + (((col >> 3) ^ (x & SW)) << 4) + (col & 4) * 2) = v;
+                }
+            }
+            lds_barrier<63>();  // staged; loads and stores may still be in flight
+            if (storer) {
+#pragma unroll
+                for (int b4 = 0; b4 < ITERS; b4 += 4) {
+                    // bytes per C row, laundered so that the offsets below
+                    // are computed here and not hoisted out of the tile loop
+                    uint32_t pitch_c = (uint32_t)N * 2u;
+                    asm volatile("" : "+s"(pitch_c)::"memory");
+#pragma unroll
+                    for (int it = b4; it < b4 + 4; ++it) {
+                        const int x = (sw % 2) * (SROWS / 2) + RPL * it + lr;  // row in the slot
+                        const u32x4_t v = *(const u32x4_t*)(rd + (RPL * it + lr) * PITCH + ((lc ^ (x & SW)) << 4));
+                        const uint32_t r0 = (uint32_t)((sw / 2) * T::WTM + h * SROWS + (sw % 2) * (SROWS / 2) + RPL * it);
+                        const uint32_t off = vbase + r0 * pitch_c;
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, kPolicyNt);
+                    }
+                }
+            }
+            lds_barrier<63>();  // both slots free again
+        }
+    };
+
+    // The whole run, compiled once for the loading waves and once for the
+    // others.
+    auto run = [&](auto ldtag) __attribute__((always_inline)) {
+        constexpr bool LD = decltype(ldtag)::value;
+        // a step's barrier: this wave's loads but the last A tile have landed
+        constexpr int VMW = LD ? T::A_LOADS : 63;
+        zero_acc();
+        // steps 0 and 1 of the first tile into slots 0 .. 3, then wait for step 0
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int l = 0; l < T::LOADS; ++l)
+                if constexpr (LD) issue_load(l < T::A_LOADS ? 2 * s : 2 * s + 1, s, l, Flag<true>{}, row_bytes);
+        lds_barrier<LD ? T::LOADS : 63>();
+#pragma unroll
+        for (int idx = 0; idx < R; ++idx) read_one(0, smem, smem + SLOT, idx);
+        int sa = 0;  // slot of the computed step's A tile; its B, then A, B, A of the next two follow
+        auto slot = [&](int i) __attribute__((always_inline)) {
+            return smem + (sa + i >= 5 ? sa + i - 5 : sa + i) * SLOT;
+        };
+        // One step: sub-step 0 loads A of step lstep into the slot after
+        // the next step's; sub-step 1 reads the next step's first fragments
+        // and loads its B into the slot this step's A leaves, unless LAST
+        // (the last step of a tile, whose epilogue needs both slots first).
+        auto step = [&](int lstep, auto masked, auto last) __attribute__((always_inline)) {
+            constexpr bool LAST = decltype(last)::value;
+            const int a2 = sa + 4 >= 5 ? sa - 1 : sa + 4;
+            substep(0, slot(0), slot(1), Flag<LD>{}, a2, lstep, 0, masked, Flag<true>{});
+            lds_barrier<VMW>();
+            substep(1, slot(2), slot(3), Flag<LD && !LAST>{}, sa, lstep, T::A_LOADS, masked, Flag<!LAST>{});
+        };
+        auto advance = [&]() __attribute__((always_inline)) { sa = sa + 2 >= 5 ? sa - 3 : sa + 2; };
+        for (;;) {
+            int ks = 0;
+            for (; ks + 2 < nfull; ++ks) {
+                step(ks + 2, Flag<false>{}, Flag<false>{});
+                advance();
+            }
+            for (; ks + 2 < nk; ++ks) {
+                step(ks + 2, Flag<true>{}, Flag<false>{});
+                advance();
+            }
+            // The last two steps load steps 0 and 1 of the next tile (after
+            // the last tile: zeros from past the end of K, into slots never
+            // read).
+            const int cm0 = m0, cn0 = n0;
+            const int next = tile + (int)gridDim.x;
+            int lbase = nk;
+            if (next < total) {
+                tile_coords(next, tiles_m, tiles_n, group_m, tm, tn);
+                m0 = tm * T::BM;
+                n0 = tn * T::BN;
+                la = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(T::BM, M - m0) * row_bytes);
+                lb = make_rsrc(B + (size_t)n0 * K, (uint32_t)min(T::BN, N - n0) * row_bytes);
+                lbase = 0;
+            }
+            step(lbase, Flag<true>{}, Flag<false>{});
+            advance();
+            step(lbase + 1, Flag<true>{}, Flag<true>{});
+            // asm MFMAs are opaque to the compiler's hazard checks: let the
+            // last ones write their accumulators before they are read
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+            // (and keep the scheduler from moving their reads above the wait)
+            __builtin_amdgcn_sched_barrier(0);
+            epilogue(slot(0), slot(1), cm0, cn0, !LD);
+            if (next >= total) break;
+            // B of the next tile's step 1 where the last step's A was
+#pragma unroll
+            for (int l = T::A_LOADS; l < T::LOADS; ++l)
+                if constexpr (LD) issue_load(sa, lbase + 1, l, Flag<true>{}, row_bytes);
+            advance();
+            zero_acc();
+#pragma unroll
+            for (int idx = 0; idx < R; ++idx) read_one(0, slot(0), slot(1), idx);
+            tile = next;
+        }
+    };
+    if (wave < T::LOADERS)
+        run(Flag<true>{});
+    else
+        run(Flag<false>{});
+    // no global->LDS load may still be writing when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 // Persistent streaming variant of the kernel above.  The grid holds one
@@ -1582,13 +1901,10 @@ struct Variant {
 
 int num_cus(int device);
 
-// Store mode of C (see kStoreNt) for a grid of `tiles` tiles.
-int c_store_mode(int64_t N, const void* C, int64_t tiles)
+// Store mode of C (see c_vec above).
+int c_store_mode(int64_t N, const void* C)
 {
-    const int vec = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 2 : ((N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0);
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    return vec | (tiles > num_cus(dev) ? kStoreNt : 0);
+    return (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 2 : ((N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0);
 }
 
 template <class T>
@@ -1597,7 +1913,7 @@ int launch_mfma(const void* A, const void* B, void* C, int64_t M, int64_t N, int
 {
     const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
-    const int c_vec = c_store_mode(N, C, tiles_m * tiles_n);
+    const int c_vec = c_store_mode(N, C);
     hipLaunchKernelGGL((gemm_nt_f16_mfma<T>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS),
                        0, stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M,
                        (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
@@ -1610,8 +1926,31 @@ int launch_ordered(const void* A, const void* B, void* C, int64_t M, int64_t N, 
 {
     const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
-    const int c_vec = c_store_mode(N, C, tiles_m * tiles_n);
+    const int c_vec = c_store_mode(N, C);
     hipLaunchKernelGGL((gemm_nt_f16_ordered<T, RS, LS, SLOTS5>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0,
+                       stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N, (int)K,
+                       (int)tiles_m, (int)tiles_n, group_m, c_vec);
+    return (int)hipGetLastError();
+}
+
+// The persistent 5-slot kernel (at most one workgroup per compute unit)
+// where its conditions hold, else the one-tile-per-workgroup 5-slot kernel.
+// Its epilogue is faster than the other's even with one tile per workgroup
+// (4096^3: +1%).
+template <class T, int RS, int LS>
+int launch_ordered_persist(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int group_m,
+                           hipStream_t stream)
+{
+    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
+    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
+    const int c_vec = c_store_mode(N, C);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const int64_t grid = std::min<int64_t>(num_cus(dev), tiles_m * tiles_n);
+    // (C offsets are 32-bit and columns past N are sent to kOob: N <= 2^22)
+    if ((c_vec & 3) != 2 || K <= T::BK || N > (int64_t(1) << 22))
+        return launch_ordered<T, RS, LS, true>(A, B, C, M, N, K, group_m, stream);
+    hipLaunchKernelGGL((gemm_nt_f16_ordered_persist<T, RS, LS>), dim3((unsigned)grid), dim3(T::THREADS), 0,
                        stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N, (int)K,
                        (int)tiles_m, (int)tiles_n, group_m, c_vec);
     return (int)hipGetLastError();
@@ -1694,8 +2033,8 @@ int launch_simple(const void* A, const void* B, void* C, int64_t M, int64_t N, i
     return (int)hipGetLastError();
 }
 
-// Variant 0 is the default for large problems; the others are kept for
-// smaller shapes and as the measured alternatives (tile shape, ring depth,
+// The variants select_mfma chooses from (kCandidates) are the defaults; the
+// others are kept as the measured alternatives (tile shape, ring depth,
 // persistence, hand-scheduled issue order).
 constexpr Variant kVariants[] = {
     {"mfma32_256x256x64_w8_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8>},
@@ -1713,6 +2052,7 @@ constexpr Variant kVariants[] = {
     {"mfma16_256x128x64_w4_s3_ordered", 256, 128, 8, launch_ordered<T256x128_k64_s3_w4_mi16, 2, 2>},
     {"mfma16_256x256x64_w8_s2_l4_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w8_l4_mi16, 2, 2>},
     {"mfma16_256x256x64_w8_r5_l4_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w8_l4_mi16, 2, 2, true>},
+    {"mfma16_256x256x64_w8_r5_l4_persistent", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2>},
     {"mfma16_256x128x64_w8_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4_mi16>},
     {"mfma16_256x128x64_w8_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w8_mi16>},
@@ -1786,12 +2126,12 @@ struct Candidate {
 
 constexpr int kCUs = 256;
 constexpr Candidate kCandidates[] = {
-    {variant_index("mfma16_256x256x64_w8_r5_l4_ordered"), 256, 256, 1300.0, 3.0},
+    {variant_index("mfma16_256x256x64_w8_r5_l4_persistent"), 256, 256, 1300.0, 3.0},
     {variant_index("mfma16_256x128x64_w8_s3_l4_ordered"), 256, 128, 1170.0, 3.0},
     {variant_index("mfma16_128x128x64_w8_s3"), 128, 128, 900.0, 3.0},
     {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 650.0, 3.0},
 };
-static_assert(variant_index("mfma16_256x256x64_w8_r5_l4_ordered") >= 0 &&
+static_assert(variant_index("mfma16_256x256x64_w8_r5_l4_persistent") >= 0 &&
                   variant_index("mfma16_256x128x64_w8_s3_l4_ordered") >= 0 &&
                   variant_index("mfma16_128x128x64_w8_s3") >= 0 && variant_index("mfma16_64x64x64_w4_s3") >= 0,
               "selected variants are in the table");

@@ -57,7 +57,8 @@ RUNGS = {
     "mfma16_256x256x64_w8_s2_l4": "16x16x32 MFMAs, 8 waves, 4 of them loading",
     "mfma16_256x256x64_w4_s2_ordered": "4 waves again, every read and load placed by hand, one per 4 MFMAs",
     "mfma16_256x256x64_w8_s2_l4_ordered": "8 waves, 4 loading, every read and load placed by hand",
-    "mfma16_256x256x64_w8_r5_l4_ordered": "same with a 5-slot ring: A loads half a step earlier, loads over the whole step: the default",
+    "mfma16_256x256x64_w8_r5_l4_ordered": "same with a 5-slot ring: A loads half a step earlier, loads over the whole step",
+    "mfma16_256x256x64_w8_r5_l4_persistent": "same, persistent: the next tile's first steps load during this tile's last, half the waves store C: the default",
     "mfma16_256x128x64_w4_s3": "16x16x32 MFMAs, 256x128 tile, 4 waves",
     "mfma16_256x128x64_w8_s3": "16x16x32 MFMAs, 256x128 tile, 8 waves",
     "mfma16_256x128x64_w4_s3_ordered": "256x128 tile, 4 waves, issue order fixed by hand",

@@ -61,10 +61,10 @@ def test_selection(lib):
         assert 0 <= v < n
         assert binding.gemm_nt_f16_config_name(w.M, w.N, w.K).startswith("mfma")
     name = binding.gemm_nt_f16_config_name
-    assert name(8192, 8192, 8192) == "mfma16_256x256x64_w8_r5_l4_ordered"
-    assert name(4096, 4096, 4096) == "mfma16_256x256x64_w8_r5_l4_ordered"
-    assert name(5000, 3000, 6000) == "mfma16_256x256x64_w8_r5_l4_ordered"
-    assert name(4096, 4096, 1024) == "mfma16_256x256x64_w8_r5_l4_ordered"
+    assert name(8192, 8192, 8192) == "mfma16_256x256x64_w8_r5_l4_persistent"
+    assert name(4096, 4096, 4096) == "mfma16_256x256x64_w8_r5_l4_persistent"
+    assert name(5000, 3000, 6000) == "mfma16_256x256x64_w8_r5_l4_persistent"
+    assert name(4096, 4096, 1024) == "mfma16_256x256x64_w8_r5_l4_persistent"
     assert name(2048, 2048, 8192) == "mfma16_128x128x64_w8_s3"
     assert name(2048, 2048, 2048) == "mfma16_128x128x64_w8_s3"
     assert name(1024, 1024, 1024) == "mfma16_64x64x64_w4_s3"

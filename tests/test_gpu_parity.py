@@ -249,12 +249,17 @@ def test_edge_shapes_every_variant():
 
 
 @pytest.mark.parametrize("M,N,K", [(5000, 6000, 72), (8192, 8192, 128), (2304, 9000, 8),
-                                   (4100, 4100, 72), (4097, 4097, 16)])
+                                   (4100, 4100, 72), (4097, 4097, 16), (4200, 4104, 200),
+                                   (2560, 8200, 328)])
 def test_many_tiles_per_workgroup_every_variant(M, N, K):
     """Shapes with more tiles than compute units, so the persistent kernels
     stream several tiles (and their K tails) through one workgroup and the
     others store C with the nontemporal hint; N = 4100 and 4097 take that
-    hint with 8-byte and single-element stores."""
+    hint with 8-byte and single-element stores.  4200 x 4104 x 200 and
+    2560 x 8200 x 328 give the persistent 5-slot kernel one or two tiles per
+    workgroup, K loops of 4 and 6 steps with a K tail, and partial tiles at
+    both M and N (N % 256 = 8: the last tile column has one 16-byte chunk per
+    row)."""
     a, b = workloads.small_integers(M, N, K, seed=M + N + K)
     _, c16 = oracle.gemm_nt(a, b)
     for name, vid in variant_ids().items():
