@@ -2126,10 +2126,10 @@ struct Candidate {
 
 constexpr int kCUs = 256;
 constexpr Candidate kCandidates[] = {
-    {variant_index("mfma16_256x256x64_w8_r5_l4_persistent"), 256, 256, 1300.0, 3.0},
-    {variant_index("mfma16_256x128x64_w8_s3_l4_ordered"), 256, 128, 1170.0, 3.0},
-    {variant_index("mfma16_128x128x64_w8_s3"), 128, 128, 900.0, 3.0},
-    {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 650.0, 3.0},
+    {variant_index("mfma16_256x256x64_w8_r5_l4_persistent"), 256, 256, 1500.0, 3.0},
+    {variant_index("mfma16_256x128x64_w8_s3_l4_ordered"), 256, 128, 1300.0, 3.0},
+    {variant_index("mfma16_128x128x64_w8_s3"), 128, 128, 1100.0, 3.0},
+    {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 730.0, 3.0},
 };
 static_assert(variant_index("mfma16_256x256x64_w8_r5_l4_persistent") >= 0 &&
                   variant_index("mfma16_256x128x64_w8_s3_l4_ordered") >= 0 &&

@@ -253,9 +253,8 @@ def test_edge_shapes_every_variant():
                                    (2560, 8200, 328)])
 def test_many_tiles_per_workgroup_every_variant(M, N, K):
     """Shapes with more tiles than compute units, so the persistent kernels
-    stream several tiles (and their K tails) through one workgroup and the
-    others store C with the nontemporal hint; N = 4100 and 4097 take that
-    hint with 8-byte and single-element stores.  4200 x 4104 x 200 and
+    stream several tiles (and their K tails) through one workgroup; N = 4100
+    and 4097 take the 8-byte and single-element stores.  4200 x 4104 x 200 and
     2560 x 8200 x 328 give the persistent 5-slot kernel one or two tiles per
     workgroup, K loops of 4 and 6 steps with a K tail, and partial tiles at
     both M and N (N % 256 = 8: the last tile column has one 16-byte chunk per

@@ -1,0 +1,34 @@
+"""Host logic of the shape sweep (no GPU): its candidate list matches the
+library's variants and its table is built from a run's JSON line."""
+from __future__ import annotations
+
+import json
+
+from dense_fp16_gemm_04_amd import binding, sweep
+
+
+def test_candidates_are_variants():
+    names = binding.variants()
+    for n in sweep.CANDIDATES:
+        assert n in names
+    for s in sweep.DEFAULT_SHAPES:
+        M, N, K = (int(t) for t in s.split("x"))
+        # every default shape takes the MFMA path (K % 8 == 0, aligned rows)
+        assert binding.gemm_nt_f16_config_name(M, N, K) in sweep.CANDIDATES
+
+
+def test_table_from_json(tmp_path, capsys):
+    t = {n: 100.0 + i for i, n in enumerate(sweep.CANDIDATES)}
+    t.update({"selected": 101.0, "hipBLASLt": 50.0})
+    row = {"shape": "64x64x64", "selected": sweep.CANDIDATES[1], "tflops": t}
+    p = tmp_path / "sweep.json"
+    p.write_text("noise\n" + json.dumps({"launches": 5, "rows": [row]}) + "\n")
+    assert sweep.table(str(p)) == 0
+    out = capsys.readouterr().out.splitlines()
+    assert out[0].startswith("| shape | selected |")
+    cells = [c.strip() for c in out[2].strip("|").split("|")]
+    assert cells[0] == "64x64x64"
+    assert cells[2] == "101"
+    best = 100.0 + len(sweep.CANDIDATES) - 1
+    assert cells[-3] == "%.2f" % (best / 101.0)
+    assert cells[-1] == "%.2f" % (101.0 / 50.0)
