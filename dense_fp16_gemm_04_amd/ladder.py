@@ -62,9 +62,11 @@ RUNGS = {
     "mfma16_256x128x64_w4_s3": "16x16x32 MFMAs, 256x128 tile, 4 waves",
     "mfma16_256x128x64_w8_s3": "16x16x32 MFMAs, 256x128 tile, 8 waves",
     "mfma16_256x128x64_w4_s3_ordered": "256x128 tile, 4 waves, issue order fixed by hand",
-    "mfma16_256x128x64_w8_s3_l4_ordered": "256x128 tile, 8 waves, 4 loading, issue order fixed by hand (default for one GPU's share)",
+    "mfma16_256x128x64_w8_s3_l4_ordered": "256x128 tile, 8 waves (2x4, 128x32 each), 4 loading, issue order fixed by hand",
+    "mfma16_256x128x64_w8x_s3_l4_ordered": "same with the waves laid out 4x2 (64x64 each: a fifth fewer LDS reads per MFMA; default for one GPU's share)",
     "mfma16_128x128x64_w4_s3": "16x16x32 MFMAs, 128x128 tile, 4 waves",
-    "mfma16_128x128x64_w8_s3": "16x16x32 MFMAs, 128x128 tile, 8 waves (default for mid sizes)",
+    "mfma16_128x128x64_w8_s3": "16x16x32 MFMAs, 128x128 tile, 8 waves",
+    "mfma16_128x128x64_w8_s3_l4_ordered": "128x128 tile, 8 waves, 4 loading, issue order fixed by hand (default for mid sizes)",
     "mfma16_64x64x64_w4_s3": "16x16x32 MFMAs, 64x64 tile (default for small sizes)",
     "mfma32_256x256x64_w4_stream": "persistent grid: the ring runs on across tile boundaries",
     "mfma32_256x256x64_w4_asm": "persistent grid with a hand-scheduled (inline asm) main loop",

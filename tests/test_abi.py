@@ -65,13 +65,18 @@ def test_selection(lib):
     assert name(4096, 4096, 4096) == "mfma16_256x256x64_w8_r5_l4_persistent"
     assert name(5000, 3000, 6000) == "mfma16_256x256x64_w8_r5_l4_persistent"
     assert name(4096, 4096, 1024) == "mfma16_256x256x64_w8_r5_l4_persistent"
-    assert name(2048, 2048, 8192) == "mfma16_128x128x64_w8_s3"
-    assert name(2048, 2048, 2048) == "mfma16_128x128x64_w8_s3"
+    assert name(2048, 2048, 8192) == "mfma16_128x128x64_w8_s3_l4_ordered"
+    assert name(2048, 2048, 2048) == "mfma16_128x128x64_w8_s3_l4_ordered"
     assert name(1024, 1024, 1024) == "mfma16_64x64x64_w4_s3"
     assert name(256, 256, 256) == "mfma16_64x64x64_w4_s3"
+    # 256-row products: 128 tiles of 128x128 leave half the CUs idle, which
+    # the model credits with a faster per-CU rate; 64x64 would take 512 tiles
+    assert name(256, 8192, 8192) == "mfma16_128x128x64_w8_s3_l4_ordered"
+    assert name(8192, 256, 8192) == "mfma16_128x128x64_w8_s3_l4_ordered"
+    assert name(1024, 1024, 8192) == "mfma16_64x64x64_w4_s3"
     # one GPU's share of an 8192^3 product split eight ways along M or N
-    assert name(1024, 8192, 8192) == "mfma16_256x128x64_w8_s3_l4_ordered"
-    assert name(8192, 1024, 8192) == "mfma16_256x128x64_w8_s3_l4_ordered"
+    assert name(1024, 8192, 8192) == "mfma16_256x128x64_w8x_s3_l4_ordered"
+    assert name(8192, 1024, 8192) == "mfma16_256x128x64_w8x_s3_l4_ordered"
     # K not a multiple of 8 cannot use the MFMA kernels
     assert binding.gemm_nt_f16_config_name(64, 64, 7).startswith("simple")
     assert lib.gemm_nt_f16_select(-1, 4, 4) == -1
