@@ -27,6 +27,7 @@ SIGNATURES = {
     "gemm_nt_f16_variant_count": ([], _i32),
     "gemm_nt_f16_variant_name": ([_i32], ctypes.c_char_p),
     "gemm_nt_f16_select": ([_i64, _i64, _i64], _i32),
+    "gemm_nt_f16_plan": ([_i64, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i32)], _i32),
     "gemm_nt_f16_config_name": ([_i64, _i64, _i64], ctypes.c_char_p),
     "gemm_nt_f16_version": ([], ctypes.c_int),
 }
@@ -81,6 +82,16 @@ def gemm_nt_f16_config_name(M: int, N: int, K: int):
 
 def gemm_nt_f16_select(M: int, N: int, K: int) -> int:
     return load().gemm_nt_f16_select(M, N, K)
+
+
+def gemm_nt_f16_plan(M: int, N: int, K: int):
+    """(variant, rows, rest): ``variant`` runs rows [0, rows) of C and, if
+    rows < M, ``rest`` runs the others (-1 otherwise); variant -1 for invalid
+    sizes."""
+    rows = ctypes.c_int64(0)
+    rest = ctypes.c_int32(0)
+    v = load().gemm_nt_f16_plan(M, N, K, ctypes.byref(rows), ctypes.byref(rest))
+    return v, rows.value, rest.value
 
 
 def _check(a, b, out):

@@ -2139,26 +2139,74 @@ static_assert(variant_index("mfma16_256x256x64_w8_r5_l4_persistent") >= 0 &&
                   variant_index("mfma16_64x64x64_w4_s3") >= 0,
               "selected variants are in the table");
 
-int select_mfma(int64_t M, int64_t N, int64_t K)
+// Modelled time of one kernel on an M x N x K product: whole waves of
+// tiles over the CUs at the kernel's sustained per-CU rate, plus a fixed
+// cost per wave.  A wave that leaves CUs idle (a grid smaller than the
+// chip, or the last wave of a larger one) runs its busy CUs faster (clock
+// and L2 headroom): measured 1.25x per CU with half of them idle.
+double model_us(const Candidate& c, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const int64_t full = tiles / kCUs, rest = tiles % kCUs;
+    const double tile_us = 2.0 * c.bm * c.bn * (double)K / (c.tflops_chip * 1e12 / kCUs) * 1e6;
+    double us = (double)full * (tile_us + c.wave_us);
+    if (rest > 0) us += tile_us / (1.0 + 0.5 * (1.0 - (double)rest / kCUs)) + c.wave_us;
+    return us;
+}
+
+int select_mfma(int64_t M, int64_t N, int64_t K, double* us_out = nullptr)
 {
     int best = kCandidates[0].variant;
     double best_us = 0;
     bool first = true;
     for (const Candidate& c : kCandidates) {
-        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-        const int64_t waves = (tiles + kCUs - 1) / kCUs;
-        double tile_us = 2.0 * c.bm * c.bn * (double)K / (c.tflops_chip * 1e12 / kCUs) * 1e6;
-        // A grid that leaves CUs idle runs its busy ones faster (clock and L2
-        // headroom): measured 1.25x per CU with half of them idle.
-        if (tiles < kCUs) tile_us /= 1.0 + 0.5 * (1.0 - (double)tiles / kCUs);
-        const double us = (double)waves * (tile_us + c.wave_us);
+        const double us = model_us(c, M, N, K);
         if (first || us < best_us) {
             best = c.variant;
             best_us = us;
             first = false;
         }
     }
+    if (us_out) *us_out = best_us;
     return best;
+}
+
+// A launch plan: `variant` on rows [0, rows) of C and, if rows < M,
+// `rest` on rows [rows, M).  When the 256 x 256 tiles of a product fill the
+// chip except for a small last wave, running whole waves of them over the
+// first rows and the remaining rows with the tile the model picks for them
+// beats any single kernel (6144^3: 1376 TFLOP/s against 1260; 4352 x 4352 x
+// 2048: 1138 against 978).  Only rows are split: C has no leading
+// dimension, so a block of whole rows is the only sub-product that is
+// itself a contiguous problem.
+struct Plan {
+    int variant;
+    int64_t rows;
+    int rest;
+};
+constexpr double kSplitUs = 4.0;  // the second launch (measured gap 2-4 us)
+
+Plan plan_mfma(int64_t M, int64_t N, int64_t K)
+{
+    double best_us = 0;
+    Plan plan{select_mfma(M, N, K, &best_us), M, -1};
+    const Candidate& big = kCandidates[0];
+    const int64_t tiles_m = (M + big.bm - 1) / big.bm, tiles_n = (N + big.bn - 1) / big.bn;
+    const int64_t waves = (tiles_m * tiles_n + kCUs - 1) / kCUs;
+    // main part: the most tile rows that fit in w whole waves, w = 1, 2, ...
+    for (int64_t w = 1; w < waves && w <= 4096; ++w) {
+        const int64_t r = w * kCUs / tiles_n;
+        if (r < 1 || r >= tiles_m) continue;
+        const int64_t rows = r * big.bm;
+        double rest_us = 0;
+        const int rest = select_mfma(M - rows, N, K, &rest_us);
+        const double us = model_us(big, rows, N, K) + rest_us + kSplitUs;
+        if (us < best_us) {
+            best_us = us;
+            plan = Plan{big.variant, rows, rest};
+        }
+    }
+    return plan;
 }
 }  // namespace
 
@@ -2176,9 +2224,19 @@ const char* gemm_nt_f16_variant_name(int32_t variant)
 
 int32_t gemm_nt_f16_select(int64_t M, int64_t N, int64_t K)
 {
+    return gemm_nt_f16_plan(M, N, K, nullptr, nullptr);
+}
+
+int32_t gemm_nt_f16_plan(int64_t M, int64_t N, int64_t K, int64_t* rows, int32_t* rest)
+{
+    if (rows) *rows = M;
+    if (rest) *rest = -1;
     if (M < 0 || N < 0 || K < 0 || M > kMaxMN || N > kMaxMN || K > kMaxMN) return -1;
     if (K % 8 != 0 || K >= kMaxK) return kSimple;
-    return select_mfma(M, N, K);
+    const Plan p = plan_mfma(M, N, K);
+    if (rows) *rows = p.rows;
+    if (rest) *rest = p.rest;
+    return p.variant;
 }
 
 const char* gemm_nt_f16_config_name(int64_t M, int64_t N, int64_t K)
@@ -2195,7 +2253,16 @@ int gemm_nt_f16_ex(const void* A, const void* B, void* C, int64_t M, int64_t N, 
     if (variant >= kNumVariants) return hipErrorInvalidValue;
     if (M == 0 || N == 0) return hipSuccess;
     const bool fast = mfma_eligible(A, B, K);
-    if (variant < 0) variant = fast ? select_mfma(M, N, K) : kSimple;
+    if (variant < 0 && fast) {
+        const Plan p = plan_mfma(M, N, K);
+        const Variant& v = kVariants[p.variant];
+        rc = v.launch(A, B, C, p.rows, N, K, v.group_m, stream);
+        if (rc != hipSuccess || p.rows == M) return rc;
+        const Variant& r = kVariants[p.rest];
+        return r.launch((const _Float16*)A + p.rows * K, B, (_Float16*)C + p.rows * N, M - p.rows, N, K,
+                        r.group_m, stream);
+    }
+    if (variant < 0) variant = kSimple;
     else if (variant != kSimple && !fast) return hipErrorInvalidValue;
     const Variant& v = kVariants[variant];
     return v.launch(A, B, C, M, N, K, v.group_m, stream);

@@ -1,7 +1,8 @@
 """Shape sweep: the selected kernel, every selectable kernel and hipBLASLt.
 
-For each shape the sweep times, in one process on one GPU, the kernel the
-library selects, each of the kernels the selection chooses from, and
+For each shape the sweep times, in one process on one GPU, what the library
+runs (one kernel, or two on blocks of rows), each of the kernels it chooses
+from run alone on the whole product, and
 hipBLASLt (``torch.matmul``, as context only), each as a CUDA-graph replay
 of back-to-back launches.  It reports TFLOP/s and which kernel was fastest,
 so the selection can be checked against measurement on square, non-square
@@ -30,7 +31,8 @@ if ROOT not in sys.path:
 DEFAULT_SHAPES = [
     "512x512x512", "1024x1024x1024", "2048x2048x2048", "3072x3072x3072", "4096x4096x4096",
     "6144x6144x6144", "8192x8192x8192", "3000x3000x3000", "5000x3000x6000", "2816x2816x4096",
-    "4352x4352x2048", "8192x8192x1024", "4096x4096x1024", "4096x4096x16384", "2048x2048x8192",
+    "4352x4352x2048", "6144x6144x2048", "4104x4096x2048", "8192x8192x1024", "4096x4096x1024",
+    "4096x4096x16384", "2048x2048x8192",
     "1024x1024x8192", "256x8192x8192", "512x8192x8192", "1024x8192x8192", "2048x8192x8192",
     "8192x256x8192", "8192x1024x8192", "8192x8192x256", "16384x4096x4096", "4096x16384x4096",
 ]
@@ -82,7 +84,7 @@ def run(args) -> int:
         a = (torch.randn(M, K, device="cuda", generator=gen) * K ** -0.25).half()
         b = (torch.randn(N, K, device="cuda", generator=gen) * K ** -0.25).half()
         out = torch.empty(M, N, dtype=torch.float16, device="cuda")
-        sel = binding.gemm_nt_f16_select(M, N, K)
+        sel, prows, rest = binding.gemm_nt_f16_plan(M, N, K)
         flop = 2.0 * M * N * K
         fns = [("selected", lambda: binding.gemm_nt_f16(a, b, out=out))]
         for vid in cand:
@@ -95,9 +97,12 @@ def run(args) -> int:
             res[label] = flop / ms / 1e9
         best = max(CANDIDATES, key=lambda n: res[n])
         row = {"shape": shape, "selected": names[sel], "tflops": res}
+        if prows < M:
+            row["split"] = {"rows": prows, "rest": names[rest]}
         rows.append(row)
-        print("sweep: %-18s selected %-40s %7.1f  best %-40s %7.1f  hipBLASLt %7.1f" % (
-            shape, names[sel], res["selected"], best, res[best], res["hipBLASLt"]), file=sys.stderr, flush=True)
+        label = names[sel] + ("" if prows == M else " rows<%d + %s" % (prows, names[rest]))
+        print("sweep: %-18s selected %-40s %7.1f  best single %-40s %7.1f  hipBLASLt %7.1f" % (
+            shape, label, res["selected"], best, res[best], res["hipBLASLt"]), file=sys.stderr, flush=True)
     print(json.dumps({"launches": args.launches, "rows": rows}), flush=True)
     return 0
 
@@ -109,13 +114,16 @@ def table(path) -> int:
     short = {n: n.replace("mfma16_", "").replace("_ordered", " ord").replace("_persistent", " pers")
              for n in CANDIDATES}
     print("| shape | selected | selected TF/s | " + " | ".join(short[n] for n in CANDIDATES)
-          + " | best / selected | hipBLASLt | selected / hipBLASLt |")
+          + " | best single / selected | hipBLASLt | selected / hipBLASLt |")
     print("|---" * (len(CANDIDATES) + 6) + "|")
     for r in data["rows"]:
         t = r["tflops"]
         best = max(t[n] for n in CANDIDATES)
+        sel = short.get(r["selected"], r["selected"])
+        if "split" in r:
+            sel += " (rows < %d) + %s" % (r["split"]["rows"], short.get(r["split"]["rest"], r["split"]["rest"]))
         print("| %s | %s | %.0f | %s | %.2f | %.0f | %.2f |" % (
-            r["shape"], short.get(r["selected"], r["selected"]), t["selected"],
+            r["shape"], sel, t["selected"],
             " | ".join("%.0f" % t[n] for n in CANDIDATES), best / t["selected"], t["hipBLASLt"],
             t["selected"] / t["hipBLASLt"]))
     return 0

@@ -55,12 +55,15 @@ typedef struct ihipStream_t* hipStream_t;
 #define GEMM_NT_F16_VERSION 1
 
 /* C = A * B^T as described above, with the kernel variant chosen from
- * (M, N, K) and the pointers' alignment. */
+ * (M, N, K) and the pointers' alignment.  When 256 x 256 tiles would leave
+ * a small last wave, the rows of C are split in two blocks, each enqueued
+ * as its own kernel on `stream` (see gemm_nt_f16_plan). */
 int gemm_nt_f16(const void* A, const void* B, void* C,
                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /* Same operation with an explicit kernel variant (0 <= variant <
- * gemm_nt_f16_variant_count()), or the automatic choice if variant < 0.
+ * gemm_nt_f16_variant_count()), run on all of C, or the automatic choice
+ * (the plan of gemm_nt_f16) if variant < 0.
  * For benchmarks and ablations.  A variant whose requirements (alignment,
  * K % 8) the arguments do not meet returns hipErrorInvalidValue. */
 int gemm_nt_f16_ex(const void* A, const void* B, void* C,
@@ -74,11 +77,21 @@ int32_t gemm_nt_f16_variant_count(void);
  * NULL for an unknown index.  The string is owned by the library. */
 const char* gemm_nt_f16_variant_name(int32_t variant);
 
-/* Index of the variant gemm_nt_f16 uses for these sizes when A and B are
- * 16-byte aligned, or -1 for invalid sizes.  Host-only; enqueues nothing. */
+/* Index of the variant gemm_nt_f16 uses for these sizes (for the first
+ * block of rows if it splits them) when A and B are 16-byte aligned, or -1
+ * for invalid sizes.  Host-only; enqueues nothing. */
 int32_t gemm_nt_f16_select(int64_t M, int64_t N, int64_t K);
 
-/* Name of that variant (NULL for invalid sizes). */
+/* The whole launch plan of gemm_nt_f16 for these sizes (A and B 16-byte
+ * aligned): returns the variant for rows [0, *rows) of C, as
+ * gemm_nt_f16_select does; *rows (if rows is not NULL) receives the number
+ * of rows it covers (M when nothing is split, else a multiple of 256) and
+ * *rest (if not NULL) the variant for rows [*rows, M), or -1.  Host-only;
+ * enqueues nothing.  -1 for invalid sizes. */
+int32_t gemm_nt_f16_plan(int64_t M, int64_t N, int64_t K, int64_t* rows,
+                         int32_t* rest);
+
+/* Name of the variant gemm_nt_f16_select returns (NULL for invalid sizes). */
 const char* gemm_nt_f16_config_name(int64_t M, int64_t N, int64_t K);
 
 /* GEMM_NT_F16_VERSION of the built library. */

@@ -144,3 +144,27 @@ def test_binding_rejects_bad_tensors():
         binding.gemm_nt_f16(a, torch.zeros((4, 9), dtype=torch.float16))
     with pytest.raises(ValueError):  # CPU tensors: no GPU path here
         binding.gemm_nt_f16(a, torch.zeros((4, 8), dtype=torch.float16))
+
+
+def test_launch_plan(lib):
+    """The row split of gemm_nt_f16 (host logic only)."""
+    names = binding.variants()
+    plan = binding.gemm_nt_f16_plan
+    # full waves of 256x256 tiles, or one wave: one kernel on all of C
+    for shape in [(8192, 8192, 8192), (4096, 4096, 4096), (12288, 12288, 4096), (5000, 3000, 6000)]:
+        v, rows, rest = plan(*shape)
+        assert (rows, rest) == (shape[0], -1), shape
+        assert v == binding.gemm_nt_f16_select(*shape)
+    # a small last wave: whole waves over the first rows, the rest apart
+    for shape in [(6144, 6144, 6144), (4352, 4352, 2048), (4104, 4096, 2048), (4200, 4352, 1024)]:
+        v, rows, rest = plan(*shape)
+        assert names[v] == "mfma16_256x256x64_w8_r5_l4_persistent", shape
+        assert 0 < rows < shape[0] and rows % 256 == 0 and 0 <= rest < len(names), shape
+        # the most whole tile rows that fit in w waves of 256 tiles
+        tiles_n = (shape[1] + 255) // 256
+        r = rows // 256
+        w = -(-r * tiles_n // 256)
+        assert (r + 1) * tiles_n > w * 256, shape
+        assert v == binding.gemm_nt_f16_select(*shape)
+    assert plan(64, 64, 7) == (binding.gemm_nt_f16_select(64, 64, 7), 64, -1)
+    assert plan(-1, 4, 4)[0] == -1

@@ -269,6 +269,21 @@ def test_many_tiles_per_workgroup_every_variant(M, N, K):
         assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), (M, N, K, name)
 
 
+@pytest.mark.parametrize("M,N,K", [(4200, 4352, 1024), (4104, 4096, 2048), (4352, 4360, 2048)])
+def test_split_launch_plan(M, N, K):
+    """Shapes whose 256x256 tiles leave a small last wave: gemm_nt_f16 runs
+    whole waves over the first rows and the remaining rows (with an M tail,
+    an N tail, or only 8 rows) as a second kernel.  Bit-exact on integer
+    inputs through the whole product."""
+    v, rows, rest = binding.gemm_nt_f16_plan(M, N, K)
+    assert 0 < rows < M and rows % 256 == 0 and rest >= 0
+    a, b = workloads.small_integers(M, N, K, seed=M * 7 + N + K)
+    _, c16 = oracle.gemm_nt(a, b)
+    print("case split", M, N, K, rows, binding.variants()[v], binding.variants()[rest], flush=True)
+    got = run(a, b)
+    assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), (M, N, K)
+
+
 def test_k_zero_many_tiles_every_variant():
     torch = _torch()
     a = torch.zeros((4096, 0), dtype=torch.float16, device=dev())

@@ -14,15 +14,18 @@ def test_candidates_are_variants():
     for s in sweep.DEFAULT_SHAPES:
         M, N, K = (int(t) for t in s.split("x"))
         # every default shape takes the MFMA path (K % 8 == 0, aligned rows)
-        assert binding.gemm_nt_f16_config_name(M, N, K) in sweep.CANDIDATES
+        v, rows, rest = binding.gemm_nt_f16_plan(M, N, K)
+        assert names[v] in sweep.CANDIDATES
+        assert rows == M or names[rest] in sweep.CANDIDATES
 
 
 def test_table_from_json(tmp_path, capsys):
     t = {n: 100.0 + i for i, n in enumerate(sweep.CANDIDATES)}
     t.update({"selected": 101.0, "hipBLASLt": 50.0})
     row = {"shape": "64x64x64", "selected": sweep.CANDIDATES[1], "tflops": t}
+    split = dict(row, shape="128x64x64", split={"rows": 64, "rest": sweep.CANDIDATES[2]})
     p = tmp_path / "sweep.json"
-    p.write_text("noise\n" + json.dumps({"launches": 5, "rows": [row]}) + "\n")
+    p.write_text("noise\n" + json.dumps({"launches": 5, "rows": [row, split]}) + "\n")
     assert sweep.table(str(p)) == 0
     out = capsys.readouterr().out.splitlines()
     assert out[0].startswith("| shape | selected |")
@@ -32,3 +35,4 @@ def test_table_from_json(tmp_path, capsys):
     best = 100.0 + len(sweep.CANDIDATES) - 1
     assert cells[-3] == "%.2f" % (best / 101.0)
     assert cells[-1] == "%.2f" % (101.0 / 50.0)
+    assert "(rows < 64)" in out[3]
