@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -86,15 +87,20 @@ def main(argv=None) -> int:
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after timing, run one plain device copy of this many MiB (a kernel of "
                         "known traffic, to scale hardware byte counters against)")
+    p.add_argument("--repeat", type=int, default=1, metavar="R",
+                   help="run the measurement in R fresh processes, one after the other, and "
+                        "report the median (the pages quote the median of three)")
     args = p.parse_args(argv)
 
     if args.gpus != 1:
         print("bench.py: this benchmark runs on one GPU only; --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         return 2
-    if args.steps < 1 or args.warmup < 0:
-        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+    if args.steps < 1 or args.warmup < 0 or args.repeat < 1:
+        print("bench.py: --steps and --repeat must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
+    if args.repeat > 1:
+        return repeated(args, argv if argv is not None else sys.argv[1:])
 
     import numpy as np
     import torch
@@ -117,13 +123,23 @@ def main(argv=None) -> int:
     tb = torch.from_numpy(b).to(dev)
     out = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     names = binding.variants()
-    vid = args.variant if args.variant >= 0 else binding.gemm_nt_f16_select(w.M, w.N, w.K)
+    if args.variant >= 0:
+        vid, rows, rest = args.variant, w.M, -1
+    else:  # the library's own plan, as gemm_nt_f16 runs it
+        vid, rows, rest = binding.gemm_nt_f16_plan(w.M, w.N, w.K)
     vname = names[vid]
-    log("bench: variant %d %s" % (vid, vname))
+    plan = vname if rows == w.M else "%s on rows [0, %d) + %s" % (vname, rows, names[rest])
+    log("bench: %s" % plan)
+
+    def step():
+        if args.variant >= 0:
+            binding.gemm_nt_f16_ex(ta, tb, out=out, variant=vid)
+        else:
+            binding.gemm_nt_f16(ta, tb, out=out)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
-        binding.gemm_nt_f16_ex(ta, tb, out=out, variant=vid)
+        step()
     torch.cuda.synchronize()
     if args.cooldown > 0:
         time.sleep(args.cooldown)
@@ -134,7 +150,7 @@ def main(argv=None) -> int:
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        binding.gemm_nt_f16_ex(ta, tb, out=out, variant=vid)
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -156,7 +172,7 @@ def main(argv=None) -> int:
         e2 = torch.cuda.Event(enable_timing=True)
         s2.record(stream)
         for _ in range(args.throttle_check):
-            binding.gemm_nt_f16_ex(ta, tb, out=out, variant=vid)
+            step()
         e2.record(stream)
         torch.cuda.synchronize()
         ms2 = s2.elapsed_time(e2) / args.throttle_check
@@ -184,7 +200,7 @@ def main(argv=None) -> int:
         "unit": "TFLOP/s",
         "frac": tflops / PEAK_TFLOPS,
         "traffic": (TRAFFIC["bytes"] if TRAFFIC and TRAFFIC["workload"] == w.name
-                    and TRAFFIC["kernel"] == vname else None),
+                    and TRAFFIC["kernel"] == vname and rows == w.M else None),
     }
     rec = {
         "metric": METRIC,
@@ -201,7 +217,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed,
                    "inputs": "iid N(0, 1/sqrt(K)) fp16, K-major", "accumulate": "f32",
-                   "output": "f16", "kernel": vname, "pct_of_peak": 100 * tflops / PEAK_TFLOPS},
+                   "output": "f16", "kernel": plan, "pct_of_peak": 100 * tflops / PEAK_TFLOPS},
         "roofline": roof,
     }
     if throttle is not None:
@@ -212,6 +228,46 @@ def main(argv=None) -> int:
         rec["cpu_baseline"] = cpu_baseline(a, b, rows)
         log("bench: oracle %.4g TFLOP/s on %d threads" % (rec["cpu_baseline"]["value"],
                                                            rec["cpu_baseline"]["cores"]))
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def repeated(args, argv) -> int:
+    """The measurement in args.repeat fresh child processes, one after the
+    other (this process never touches the GPU); the record of the median
+    run, with every run's value beside it."""
+    child = []
+    skip = False
+    for x in argv:  # drop --repeat and --cpu-rows from the child's arguments
+        if skip:
+            skip = False
+            continue
+        if x in ("--repeat", "--cpu-rows"):
+            skip = True
+            continue
+        if x.startswith("--repeat=") or x.startswith("--cpu-rows="):
+            continue
+        child.append(x)
+    recs = []
+    for i in range(args.repeat):
+        log("bench: process %d of %d" % (i + 1, args.repeat))
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), *child, "--repeat", "1",
+                              "--cpu-rows", "0"], stdout=subprocess.PIPE, text=True)
+        if res.returncode != 0:
+            print("bench.py: run %d failed (%d)" % (i + 1, res.returncode), file=sys.stderr)
+            return res.returncode
+        recs.append(json.loads(res.stdout.strip().splitlines()[-1]))
+    values = [r["value"] for r in recs]
+    rec = sorted(recs, key=lambda r: r["value"])[len(recs) // 2]
+    rec["repeat"] = {"processes": args.repeat, "values": values, "range": [min(values), max(values)],
+                     "reported": "median"}
+    if args.cpu_rows > 0:
+        from dense_fp16_gemm_04_amd import workloads
+        w = workloads.by_name(args.workload)
+        a, b = workloads.workload_inputs(w)
+        rows = min(args.cpu_rows, w.M)
+        log("bench: timing the CPU oracle on %d rows ..." % rows)
+        rec["cpu_baseline"] = cpu_baseline(a, b, rows)
     print(json.dumps(rec), flush=True)
     return 0
 
