@@ -2126,7 +2126,6 @@ struct Candidate {
     double wave_us;      // fixed cost per wave of tiles
 };
 
-constexpr int kCUs = 256;
 constexpr Candidate kCandidates[] = {
     {variant_index("mfma16_256x256x64_w8_r5_l4_persistent"), 256, 256, 1500.0, 3.0},
     {variant_index("mfma16_256x128x64_w8x_s3_l4_ordered"), 256, 128, 1330.0, 3.0},
@@ -2144,23 +2143,27 @@ static_assert(variant_index("mfma16_256x256x64_w8_r5_l4_persistent") >= 0 &&
 // cost per wave.  A wave that leaves CUs idle (a grid smaller than the
 // chip, or the last wave of a larger one) runs its busy CUs faster (clock
 // and L2 headroom): measured 1.25x per CU with half of them idle.
-double model_us(const Candidate& c, int64_t M, int64_t N, int64_t K)
+// The rates are for MI355X's 256 CUs; `cus` is the device's count (fewer
+// in a partition mode), and the per-CU rate is kept.
+constexpr int kRateCUs = 256;
+
+double model_us(const Candidate& c, int64_t M, int64_t N, int64_t K, int cus)
 {
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const int64_t full = tiles / kCUs, rest = tiles % kCUs;
-    const double tile_us = 2.0 * c.bm * c.bn * (double)K / (c.tflops_chip * 1e12 / kCUs) * 1e6;
+    const int64_t full = tiles / cus, rest = tiles % cus;
+    const double tile_us = 2.0 * c.bm * c.bn * (double)K / (c.tflops_chip * 1e12 / kRateCUs) * 1e6;
     double us = (double)full * (tile_us + c.wave_us);
-    if (rest > 0) us += tile_us / (1.0 + 0.5 * (1.0 - (double)rest / kCUs)) + c.wave_us;
+    if (rest > 0) us += tile_us / (1.0 + 0.5 * (1.0 - (double)rest / cus)) + c.wave_us;
     return us;
 }
 
-int select_mfma(int64_t M, int64_t N, int64_t K, double* us_out = nullptr)
+int select_mfma(int64_t M, int64_t N, int64_t K, int cus, double* us_out = nullptr)
 {
     int best = kCandidates[0].variant;
     double best_us = 0;
     bool first = true;
     for (const Candidate& c : kCandidates) {
-        const double us = model_us(c, M, N, K);
+        const double us = model_us(c, M, N, K, cus);
         if (first || us < best_us) {
             best = c.variant;
             best_us = us;
@@ -2188,19 +2191,22 @@ constexpr double kSplitUs = 4.0;  // the second launch (measured gap 2-4 us)
 
 Plan plan_mfma(int64_t M, int64_t N, int64_t K)
 {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const int cus = num_cus(dev);
     double best_us = 0;
-    Plan plan{select_mfma(M, N, K, &best_us), M, -1};
+    Plan plan{select_mfma(M, N, K, cus, &best_us), M, -1};
     const Candidate& big = kCandidates[0];
     const int64_t tiles_m = (M + big.bm - 1) / big.bm, tiles_n = (N + big.bn - 1) / big.bn;
-    const int64_t waves = (tiles_m * tiles_n + kCUs - 1) / kCUs;
+    const int64_t waves = (tiles_m * tiles_n + cus - 1) / cus;
     // main part: the most tile rows that fit in w whole waves, w = 1, 2, ...
     for (int64_t w = 1; w < waves && w <= 4096; ++w) {
-        const int64_t r = w * kCUs / tiles_n;
+        const int64_t r = w * cus / tiles_n;
         if (r < 1 || r >= tiles_m) continue;
         const int64_t rows = r * big.bm;
         double rest_us = 0;
-        const int rest = select_mfma(M - rows, N, K, &rest_us);
-        const double us = model_us(big, rows, N, K) + rest_us + kSplitUs;
+        const int rest = select_mfma(M - rows, N, K, cus, &rest_us);
+        const double us = model_us(big, rows, N, K, cus) + rest_us + kSplitUs;
         if (us < best_us) {
             best_us = us;
             plan = Plan{big.variant, rows, rest};
