@@ -111,6 +111,21 @@ def test_workload_full_parity(name):
     print("%s: max %.3g mean %.3g" % (name, err.max(), err.mean()))
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 2048), (256, 8192, 4096), (4352, 4352, 2048)])
+def test_plan_shapes_gaussian(M, N, K):
+    """Unit-variance outputs through gemm_nt_f16 on shapes whose plan uses
+    the 128x128 hand-ordered kernel (2048^3; the 256-row product) or splits
+    the rows of C (4352 x 4352 x 2048), against the oracle at the same bar
+    as the workloads."""
+    v, rows, rest = binding.gemm_nt_f16_plan(M, N, K)
+    names = binding.variants()
+    print("case plan", M, N, K, names[v], rows, names[rest] if rest >= 0 else "-", flush=True)
+    a, b = workloads.gaussian(M, N, K, seed=M + 3 * N + 7 * K)
+    c64, c16 = oracle.gemm_nt(a, b)
+    err = assert_close(run(a, b), c64, c16, K, "%dx%dx%d" % (M, N, K))
+    print("max %.3g mean %.3g" % (err.max(), err.mean()))
+
+
 def test_headline_sampled_parity_and_error_figures():
     """M = N = K = 8192 in the launch configuration the benchmark times.
 
