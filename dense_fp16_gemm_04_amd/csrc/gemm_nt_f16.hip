@@ -7,8 +7,10 @@
 // mbarriers and warp-group MMA; none of those exist on CDNA4, so the kernels
 // keep only the ideas that still hold and re-derive the rest for gfx950:
 //
-//  * one workgroup per BM x BN output tile, K walked in BK-deep steps
-//    ("0. A Minimal Hopper Matmul", "Block Tiling");
+//  * a BM x BN output tile per workgroup at a time, K walked in BK-deep
+//    steps ("0. A Minimal Hopper Matmul", "Block Tiling"); the default
+//    256 x 256 kernel keeps one workgroup per CU walking its tiles, and the
+//    host may split the rows of C over two kernels (plan_mfma);
 //  * a multi-stage shared-memory ring so loads of later steps overlap the
 //    matrix-core work of the current one ("3. Warp Specialization",
 //    introduction and "Draining the Pipeline").  On CDNA4 every wave issues
@@ -28,7 +30,8 @@
 //    lane (one wave per SIMD), or 8 waves x 128 (two per SIMD).
 //
 // LDS layout of one stage: the A tile (BM rows) then the B tile (BN rows);
-// each row holds BK fp16 (64 or 128 bytes) as 16-byte chunks.  gfx950's LDS
+// the 5-slot kernels keep one operand tile per 32 KiB slot instead.  Each
+// row holds BK fp16 (64 or 128 bytes) as 16-byte chunks.  gfx950's LDS
 // serves 64 banks x 4 bytes per cycle; a 16-byte read (ds_read_b128) takes
 // four passes of 16 lanes, and the lanes of one pass must hit 16 different
 // 16-byte bank groups.  The passes are lanes {0-3, 12-15, 20-23, 24-27},
