@@ -1,5 +1,6 @@
 """Host logic of bench.py (no GPU): the one-GPU guard, argument checks and
-the fresh-process repeat that reports the median run."""
+the fresh-process repeat that reports the median run, and the amd-smi clock
+sampler (run against a stand-in amd-smi script)."""
 from __future__ import annotations
 
 import json
@@ -42,3 +43,57 @@ def test_repeat_reports_the_median_run(monkeypatch, capsys):
         assert cmd.count("--repeat") == 1 and cmd[cmd.index("--repeat") + 1] == "1"
         assert cmd[cmd.index("--cpu-rows") + 1] == "0"
         assert "--steps" in cmd and cmd[cmd.index("--steps") + 1] == "5"
+
+
+FAKE_SMI = r'''
+import json, sys
+if sys.argv[1] == "list":
+    print("noise before the document")
+    print(json.dumps([{"gpu": 0, "bdf": "0000:75:00.0"}, {"gpu": 1, "bdf": "0000:05:00.0"}]))
+else:
+    clock = lambda mhz: {"clk": {"value": mhz, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"}}
+    gpu = lambda i, base, w: {"gpu": i, "power": {"socket_power": {"value": w, "unit": "W"}},
+                              "clock": {"gfx_0": clock(base), "gfx_1": clock(base + 20), "mem_0": clock(2000),
+                                        "fclk_0": {"clk": "N/A"}}}
+    print(json.dumps({"gpu_data": [gpu(0, 1500, 1300), gpu(1, 100, 200)]}))
+'''
+
+
+def test_clock_sampler_protocol(tmp_path):
+    """The sampler waits for a first line, queries until a second one, and
+    reports every GPU's mean engine clock over the XCDs and its power;
+    samples_of picks the GPU by PCI address."""
+    script = tmp_path / "amdsmi_cli.py"
+    script.write_text(FAKE_SMI)
+    script.chmod(0o755)
+    (tmp_path / "amd-smi").symlink_to(script)
+    env = dict(__import__("os").environ, PATH="%s:%s" % (tmp_path, __import__("os").environ.get("PATH", "")))
+    proc = subprocess.Popen([sys.executable, bench.__file__, "--smi-sampler"], stdin=subprocess.PIPE,
+                            stdout=subprocess.PIPE, text=True, env=env)
+    proc.stdin.write("start\n")
+    proc.stdin.flush()
+    import time
+    time.sleep(1.0)
+    proc.stdin.write("stop\n")
+    proc.stdin.flush()
+    got = json.loads(proc.communicate(timeout=60)[0].strip().splitlines()[-1])
+    assert proc.returncode == 0
+    assert got["bdf"] == {"0": "0000:75:00.0", "1": "0000:05:00.0"}
+    assert len(got["samples"]) >= 2
+    mine = bench.samples_of(got, 0, 0x75)
+    assert mine and all(m == (1510.0, 1300.0) for m in mine)
+    assert all(m == (110.0, 200.0) for m in bench.samples_of(got, 0, 0x05))
+    assert bench.samples_of(got, 0, 0x99) == []
+
+
+def test_clock_sampler_without_a_start_line_exits():
+    proc = subprocess.run([sys.executable, bench.__file__, "--smi-sampler"], input="", stdout=subprocess.PIPE,
+                          text=True, timeout=60)
+    assert proc.returncode == 0 and proc.stdout == ""
+
+
+def test_profiler_runs_skip_the_clock_window(monkeypatch):
+    monkeypatch.delenv("ROCPROF_OUTPUT_PATH", raising=False)
+    base = bench.under_profiler()
+    monkeypatch.setenv("ROCPROF_OUTPUT_PATH", "/tmp/x")
+    assert bench.under_profiler() and not base
