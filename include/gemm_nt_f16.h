@@ -24,20 +24,25 @@
  * caller.  The library allocates no memory, keeps no per-call state and never
  * synchronizes the host; every call only enqueues kernels on `stream` (0 is
  * the null stream) and returns.  C is valid once that stream has reached the
- * point of the call.  Calls from several host threads are safe.
+ * point of the call.  Calls from several host threads are safe.  Because a
+ * call is nothing but kernel launches (no allocation, no memset, no
+ * synchronization), it may be captured into a HIP graph; each replay then
+ * reads A and B and writes C at the addresses given at capture.
  *
  * Errors: every entry point returns a hipError_t value as int: 0
  * (hipSuccess) or an error.  Argument errors return 1 (hipErrorInvalidValue)
  * before anything is enqueued: a negative dimension, a null pointer with a
  * non-zero extent, C overlapping A or B, a dimension beyond the supported
- * range (M, N < 2^31, K < 2^22, tile count < 2^31), or an unknown variant.
+ * range (M, N, K < 2^31, tile count < 2^31), or an unknown variant.
  * A failed launch returns the runtime's error code.  M == 0 or N == 0 writes
  * nothing and succeeds; K == 0 writes +0 to every element of C.
  *
- * Alignment: any 2-byte aligned pointers are accepted.  The MFMA kernels need
- * 16-byte aligned A and B and K % 8 == 0 (so every row starts on 16 bytes);
- * other inputs run a plain per-element kernel that gives the same results
- * within fp32 rounding, only slower.
+ * Alignment and size: any 2-byte aligned pointers are accepted.  The MFMA
+ * kernels need 16-byte aligned A and B, K % 8 == 0 (so every row starts on
+ * 16 bytes) and K < 2^22 (a 256-row operand tile then spans less than 2^31
+ * bytes, the reach of their 32-bit buffer offsets); other inputs run a plain
+ * per-element kernel that gives the same results within fp32 rounding, only
+ * slower.  gemm_nt_f16_ex refuses an MFMA variant for such inputs.
  */
 #ifndef GEMM_NT_F16_H
 #define GEMM_NT_F16_H
@@ -65,7 +70,7 @@ int gemm_nt_f16(const void* A, const void* B, void* C,
  * gemm_nt_f16_variant_count()), run on all of C, or the automatic choice
  * (the plan of gemm_nt_f16) if variant < 0.
  * For benchmarks and ablations.  A variant whose requirements (alignment,
- * K % 8) the arguments do not meet returns hipErrorInvalidValue. */
+ * K % 8, K < 2^22) the arguments do not meet returns hipErrorInvalidValue. */
 int gemm_nt_f16_ex(const void* A, const void* B, void* C,
                    int64_t M, int64_t N, int64_t K, int32_t variant,
                    hipStream_t stream);

@@ -406,6 +406,39 @@ def test_repeated_launches_are_deterministic_and_finite():
         assert torch.equal(o.view(torch.int16), first.view(torch.int16))
 
 
+def test_graph_replays_match_eager_calls():
+    """gemm_nt_f16 captured in a HIP graph (through torch.cuda.graph), one
+    launch and a split plan of two: before each replay new inputs are copied
+    in eagerly and an eager call computes the reference; every replay must
+    equal it bit for bit, and the oracle on integer inputs."""
+    torch = _torch()
+    for (M, N, K) in [(1000, 520, 264), (4352, 4352, 2048)]:
+        ta = torch.empty((M, K), dtype=torch.float16, device=dev())
+        tb = torch.empty((N, K), dtype=torch.float16, device=dev())
+        out = torch.empty((M, N), dtype=torch.float16, device=dev())
+        ref = torch.empty_like(out)
+        binding.gemm_nt_f16(ta.zero_(), tb.zero_(), out=out)  # eager first: the plan's CU count is cached
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            binding.gemm_nt_f16(ta, tb, out=out)
+        for r in range(4):
+            print("case graph", M, N, K, "replay", r, flush=True)
+            a, b = workloads.small_integers(M, N, K, seed=9000 + 10 * r + (M > 2000))
+            ta.copy_(torch.from_numpy(a))
+            tb.copy_(torch.from_numpy(b))
+            out.fill_(float("nan"))
+            binding.gemm_nt_f16(ta, tb, out=ref)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (M, N, K, r)
+            if M * N * K <= 1 << 28:
+                _, c16 = oracle.gemm_nt(a, b)
+                assert np.array_equal(out.cpu().numpy().view(np.uint16), c16.view(np.uint16)), (M, N, K, r)
+        del g
+
+
 def test_non_default_stream():
     torch = _torch()
     a, b = workloads.gaussian(520, 390, 264, seed=43)
