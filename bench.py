@@ -78,6 +78,37 @@ def cpu_baseline(a, b, rows: int):
     }
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_configs():
+    """The oracle on every workload of five configurations, whole products,
+    on this host's cores (capped as for the baseline), and on one thread for
+    the two smallest: wall time and GFLOP/s each."""
+    import oracle
+    from dense_fp16_gemm_04_amd import workloads
+
+    threads = cpu_threads()
+    rows = []
+    for w in workloads.WORKLOADS[:5]:
+        a, b = workloads.workload_inputs(w)
+        for t in ([threads, 1] if w.M * w.N * w.K <= 1 << 30 else [threads]):
+            t0 = time.perf_counter()
+            oracle.gemm_nt(a, b, threads=t)
+            dt = time.perf_counter() - t0
+            rows.append({"workload": w.name, "threads": t, "seconds": dt, "gflops": w.flops / dt / 1e9})
+            log("bench: oracle on %s, %d thread(s): %.3f s, %.2f GFLOP/s" % (w.name, t, dt, w.flops / dt / 1e9))
+    return {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "threads": threads, "runs": rows}
+
+
 def under_profiler() -> bool:
     """True inside rocprofv3 (which sets ROCPROF_* variables): its preloaded
     library follows every child process, so the clock window, which starts
@@ -224,6 +255,9 @@ def main(argv=None) -> int:
     p.add_argument("--repeat", type=int, default=1, metavar="R",
                    help="run the measurement in R fresh processes, one after the other, and "
                         "report the median (the pages quote the median of three)")
+    p.add_argument("--cpu-configs", action="store_true",
+                   help="also time the oracle on every configuration (whole products; about a minute "
+                        "more): cpu_baseline.per_config")
     p.add_argument("--smi-sampler", action="store_true", help=argparse.SUPPRESS)
     args = p.parse_args(argv)
     if args.smi_sampler:
@@ -390,6 +424,8 @@ def measure(args, sampler) -> int:
         rec["cpu_baseline"] = cpu_baseline(a, b, rows)
         log("bench: oracle %.4g TFLOP/s on %d threads" % (rec["cpu_baseline"]["value"],
                                                            rec["cpu_baseline"]["cores"]))
+        if args.cpu_configs:
+            rec["cpu_baseline"]["per_config"] = cpu_configs()
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -430,6 +466,8 @@ def repeated(args, argv) -> int:
         rows = min(args.cpu_rows, w.M)
         log("bench: timing the CPU oracle on %d rows ..." % rows)
         rec["cpu_baseline"] = cpu_baseline(a, b, rows)
+        if args.cpu_configs:
+            rec["cpu_baseline"]["per_config"] = cpu_configs()
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -97,3 +97,18 @@ def test_profiler_runs_skip_the_clock_window(monkeypatch):
     base = bench.under_profiler()
     monkeypatch.setenv("ROCPROF_OUTPUT_PATH", "/tmp/x")
     assert bench.under_profiler() and not base
+
+
+def test_cpu_configs_table(monkeypatch):
+    """The oracle timing table: every configuration on the host's threads,
+    the small ones on one thread too, with the CPU named."""
+    from dense_fp16_gemm_04_amd import workloads
+
+    small = tuple(workloads.Workload("w%d" % i, m, n, k, 100 + i)
+                  for i, (m, n, k) in enumerate([(16, 8, 8), (24, 16, 32), (40, 8, 16)]))
+    monkeypatch.setattr(workloads, "WORKLOADS", small)
+    t = bench.cpu_configs()
+    assert t["threads"] >= 1 and t["nproc"] >= 1 and isinstance(t["cpu_model"], str)
+    assert [(r["workload"], r["threads"]) for r in t["runs"]] == [
+        (w.name, th) for w in small for th in ([t["threads"], 1])]
+    assert all(r["seconds"] > 0 and r["gflops"] > 0 for r in t["runs"])
