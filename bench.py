@@ -233,6 +233,7 @@ def clock_window(sampler, seconds, step, stream, flops, props):
         "at that clock" % (seconds, tflops, mhz, rec["power_w_mean"], rec["pct_of_peak_at_sclk"]))
     return rec
 
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -291,7 +292,6 @@ def main(argv=None) -> int:
 
 
 def measure(args, sampler) -> int:
-    import numpy as np
     import torch
 
     from dense_fp16_gemm_04_amd import binding, workloads

@@ -2,7 +2,6 @@
 declares, and rejects bad arguments on the host before enqueuing anything."""
 from __future__ import annotations
 
-import ctypes
 import os
 import re
 
