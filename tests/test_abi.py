@@ -145,6 +145,37 @@ def test_binding_rejects_bad_tensors():
         binding.gemm_nt_f16(a, torch.zeros((4, 8), dtype=torch.float16))
 
 
+def test_launch_plan_invariants_on_random_shapes(lib):
+    """Over 2000 seeded random shapes: a plan is one kernel on all rows, or a
+    256x256 kernel on the most whole tile rows whose tiles fit in some number
+    of waves over the chip's 256 CUs, plus a kernel the model picks (possibly
+    the same one) on the rest."""
+    import numpy as np
+
+    names = binding.variants()
+    g = np.random.Generator(np.random.PCG64(2024))
+    splits = 0
+    for _ in range(2000):
+        M, N = (int(x) for x in g.integers(1, 20000, size=2))
+        K = int(g.choice([8, 64, 72, 256, 1000, 1024, 2048, 4096, 6000, 8192]))
+        v, rows, rest = binding.gemm_nt_f16_plan(M, N, K)
+        assert 0 <= v < len(names) and names[v] != "simple_f32_per_element", (M, N, K)
+        assert v == binding.gemm_nt_f16_select(M, N, K)
+        if rest == -1:
+            assert rows == M, (M, N, K)
+            continue
+        splits += 1
+        assert names[v] == "mfma16_256x256x64_w8_r5_l4_persistent", (M, N, K)
+        assert 0 < rows < M and rows % 256 == 0, (M, N, K, rows)
+        assert 0 <= rest < len(names) and names[rest] != "simple_f32_per_element", (M, N, K)
+        # w waves hold the first rows' tiles, and one more tile row would not fit
+        tiles_n = (N + 255) // 256
+        r = rows // 256
+        w = -(-r * tiles_n // 256)
+        assert r * tiles_n <= w * 256 < (r + 1) * tiles_n, (M, N, K, rows)
+    assert splits > 0
+
+
 def test_launch_plan(lib):
     """The row split of gemm_nt_f16 (host logic only)."""
     names = binding.variants()

@@ -299,6 +299,34 @@ def test_split_launch_plan(M, N, K):
     assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), (M, N, K)
 
 
+def _random_plan_shapes():
+    """16 seeded random shapes, 8 whose plan splits the rows of C and 8 run
+    as one kernel, each at most 3e10 multiply-adds (a few seconds of the
+    oracle)."""
+    g = np.random.Generator(np.random.PCG64(77))
+    split, single = [], []
+    while len(split) < 8 or len(single) < 8:
+        M, N = (int(x) for x in g.integers(1, 7000, size=2))
+        K = int(g.choice([8, 72, 136, 520, 1032, 2056]))
+        if M * N * K > 3e10:
+            continue
+        _, rows, rest = binding.gemm_nt_f16_plan(M, N, K)
+        (split if rest >= 0 else single).append((M, N, K))
+    return split[:8] + single[:8]
+
+
+def test_random_shapes_through_the_launch_plan():
+    """Integer inputs, bit-exact, through gemm_nt_f16 (the plan the library
+    makes for each shape, split or not)."""
+    for i, (M, N, K) in enumerate(_random_plan_shapes()):
+        v, rows, rest = binding.gemm_nt_f16_plan(M, N, K)
+        print("case random", M, N, K, binding.variants()[v], rows, rest, flush=True)
+        a, b = workloads.small_integers(M, N, K, seed=5000 + i)
+        _, c16 = oracle.gemm_nt(a, b)
+        got = run(a, b)
+        assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), (M, N, K, v, rows, rest)
+
+
 def test_k_zero_many_tiles_every_variant():
     torch = _torch()
     a = torch.zeros((4096, 0), dtype=torch.float16, device=dev())
