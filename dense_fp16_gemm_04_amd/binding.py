@@ -125,10 +125,12 @@ def gemm_nt_f16(a, b, out=None):
 
     Enqueued on the current stream of a's device; returns ``out``.
     """
+    import torch
     out = _check(a, b, out)
     M, K = a.shape
     N = b.shape[0]
-    rc = load().gemm_nt_f16(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, _stream(a))
+    with torch.cuda.device(a.device):  # the library plans for the current device
+        rc = load().gemm_nt_f16(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, _stream(a))
     if rc != 0:
         raise GemmError("gemm_nt_f16", rc)
     return out
@@ -136,11 +138,13 @@ def gemm_nt_f16(a, b, out=None):
 
 def gemm_nt_f16_ex(a, b, out=None, variant: int = -1):
     """``gemm_nt_f16`` with an explicit kernel variant (index into ``variants()``)."""
+    import torch
     out = _check(a, b, out)
     M, K = a.shape
     N = b.shape[0]
-    rc = load().gemm_nt_f16_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, int(variant),
-                               _stream(a))
+    with torch.cuda.device(a.device):
+        rc = load().gemm_nt_f16_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, int(variant),
+                                   _stream(a))
     if rc != 0:
         raise GemmError("gemm_nt_f16_ex", rc)
     return out
