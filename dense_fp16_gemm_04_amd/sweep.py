@@ -10,11 +10,13 @@ and skinny shapes (the pages warn that their kernels were tuned for one
 shape: "6. Four Consumers, FP16 Accumulation, and a TMA Epilogue", section
 "Performance", the closing caution).  A caller who wants the fastest kernel
 for a shape the selection gets wrong can pass the reported variant to
-``gemm_nt_f16_ex``.
+``gemm_nt_f16_ex``; ``autotune`` (or ``--autotune MxNxK``) measures that
+choice for one shape.
 
 Run (needs a GPU):
 
     python -m dense_fp16_gemm_04_amd.sweep [--shapes 8192x8192x8192,...] [--launches 50]
+    python -m dense_fp16_gemm_04_amd.sweep --autotune 6144x6144x2048
 """
 from __future__ import annotations
 
@@ -63,6 +65,47 @@ def time_graph(torch, fn, launches):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / launches
+
+
+def autotune(M: int, N: int, K: int, launches: int = 20, repeats: int = 3):
+    """Measure which way of running an M x N x K product is fastest here.
+
+    Times the library's own plan (``gemm_nt_f16``) and each kernel it
+    chooses from, run alone on the whole product through ``gemm_nt_f16_ex``,
+    on seeded random fp16 inputs of the shape: graph replays of `launches`
+    back-to-back calls, alternating between the contenders, `repeats` times,
+    keeping each one's best.  Returns ``(variant, ms)``: variant -1 when the
+    plan is fastest (call ``gemm_nt_f16``), else the index to pass to
+    ``gemm_nt_f16_ex``; ``ms`` maps each contender's name ("plan" for the
+    plan) to its best time per launch in milliseconds.
+    """
+    import torch
+
+    from dense_fp16_gemm_04_amd import binding
+
+    binding.load()
+    if not torch.cuda.is_available():
+        raise RuntimeError("autotune needs a GPU")
+    if M < 1 or N < 1 or K < 1:
+        raise ValueError("autotune needs M, N, K >= 1")
+    names = binding.variants()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(M * 31 + N * 7 + K)
+    a = (torch.randn(M, K, device="cuda", generator=gen) * K ** -0.25).half()
+    b = (torch.randn(N, K, device="cuda", generator=gen) * K ** -0.25).half()
+    out = torch.empty(M, N, dtype=torch.float16, device="cuda")
+    fns = {"plan": lambda: binding.gemm_nt_f16(a, b, out=out)}
+    if K % 8 == 0 and K < (1 << 22):  # the MFMA kernels' requirements
+        for n in CANDIDATES:
+            fns[n] = (lambda v: lambda: binding.gemm_nt_f16_ex(a, b, out=out, variant=v))(names.index(n))
+    time_graph(torch, fns["plan"], launches)  # the first graph of a shape runs slow
+    ms = {}
+    for _ in range(max(1, repeats)):
+        for label, fn in fns.items():
+            t = time_graph(torch, fn, launches)
+            ms[label] = min(ms.get(label, t), t)
+    best = min(ms, key=ms.get)
+    return (-1 if best == "plan" else names.index(best)), ms
 
 
 def run(args) -> int:
@@ -134,9 +177,18 @@ def main(argv=None) -> int:
     p.add_argument("--shapes", default=",".join(DEFAULT_SHAPES))
     p.add_argument("--launches", type=int, default=50)
     p.add_argument("--table", metavar="JSON", help="print a markdown table from a run's JSON output")
+    p.add_argument("--autotune", metavar="MxNxK",
+                   help="time the plan and each kernel on this shape; print the fastest as JSON")
     args = p.parse_args(argv)
     if args.table:
         return table(args.table)
+    if args.autotune:
+        M, N, K = (int(t) for t in args.autotune.split("x"))
+        variant, ms = autotune(M, N, K, launches=args.launches)
+        print(json.dumps({"shape": args.autotune, "variant": variant,
+                          "use": "gemm_nt_f16" if variant < 0 else "gemm_nt_f16_ex(variant=%d)" % variant,
+                          "ms": ms}), flush=True)
+        return 0
     return run(args)
 
 

@@ -1,10 +1,14 @@
-"""Host logic of the shape sweep (no GPU): its candidate list matches the
-library's variants and its table is built from a run's JSON line."""
+"""The shape sweep: its candidate list matches the library's variants and
+its table is built from a run's JSON line (host logic, no GPU); autotune
+picks a way of running a shape whose result matches the oracle (GPU)."""
 from __future__ import annotations
 
 import json
 
-from dense_fp16_gemm_04_amd import binding, sweep
+import numpy as np
+import pytest
+
+from dense_fp16_gemm_04_amd import binding, sweep, workloads
 
 
 def test_candidates_are_variants():
@@ -36,3 +40,23 @@ def test_table_from_json(tmp_path, capsys):
     assert cells[-3] == "%.2f" % (best / 101.0)
     assert cells[-1] == "%.2f" % (101.0 / 50.0)
     assert "(rows < 64)" in out[3]
+
+
+@pytest.mark.gpu
+def test_autotune_choice_is_correct():
+    import torch
+
+    import oracle
+
+    M, N, K = 1000, 520, 264
+    variant, ms = sweep.autotune(M, N, K, launches=5, repeats=2)
+    names = binding.variants()
+    assert set(ms) == {"plan", *sweep.CANDIDATES} and all(t > 0 for t in ms.values())
+    assert variant == -1 or names[variant] in sweep.CANDIDATES
+    assert ms["plan" if variant < 0 else names[variant]] == min(ms.values())
+    a, b = workloads.small_integers(M, N, K, seed=31)
+    _, c16 = oracle.gemm_nt(a, b)
+    ta, tb = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    c = binding.gemm_nt_f16(ta, tb) if variant < 0 else binding.gemm_nt_f16_ex(ta, tb, variant=variant)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cpu().numpy().view(np.uint16), c16.view(np.uint16))
