@@ -989,19 +989,25 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
                              : "memory");
     };
 
+    // fragment read `idx` of set `set`, in the order the MFMAs below first
+    // need them: B block 0, A blocks 0 .. FM-1, B blocks 1 .. FN-1
     auto read_one = [&](int set, const unsigned char* abase, const unsigned char* bbase, int idx)
                         __attribute__((always_inline)) {
         const unsigned char* pa = abase + a_row0 * T::ROW_BYTES + fr_pos[set];
         const unsigned char* pb = bbase + b_row0 * T::ROW_BYTES + fr_pos[set];
         if (idx == 0)
-            fa[set][0] = *(const half8_t*)pa;
-        else if (idx <= T::FN)
-            fb[set][idx - 1] = *(const half8_t*)(pb + (idx - 1) * T::MI * T::ROW_BYTES);
+            fb[set][0] = *(const half8_t*)pb;
+        else if (idx <= T::FM)
+            fa[set][idx - 1] = *(const half8_t*)(pa + (idx - 1) * T::MI * T::ROW_BYTES);
         else
-            fa[set][idx - T::FN] = *(const half8_t*)(pa + (idx - T::FN) * T::MI * T::ROW_BYTES);
+            fb[set][idx - T::FM] = *(const half8_t*)(pb + (idx - T::FM) * T::MI * T::ROW_BYTES);
     };
     // MFMAs of sub-step cs, with (if RD) the fragment reads of sub-step 1 -
     // cs and (if LD) loads l0 .. l0 + A_LOADS - 1 of step lstep interleaved.
+    // The MFMAs go down the columns of blocks (block row i = t % FM, column
+    // j = t / FM), so each run of FM of them shares one B fragment; that
+    // order ran 0.3-1.1% faster than along the rows (runs of FN sharing an A
+    // fragment) in alternating replays at 8192^3 and 4096 x 4096 x 16384.
     auto substep = [&](int cs, const unsigned char* ra_base, const unsigned char* rb_base, auto ld, int where,
                        int lstep, int l0, auto masked, auto rd) __attribute__((always_inline)) {
         constexpr bool LD = decltype(ld)::value, RD = decltype(rd)::value;
@@ -1009,7 +1015,7 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
         asm volatile("" : "+s"(rbytes));
 #pragma unroll
         for (int t = 0; t < G; ++t) {
-            mfma16_agpr(acc[t / T::FN][t % T::FN], fb[cs][t % T::FN], fa[cs][t / T::FN]);
+            mfma16_agpr(acc[t % T::FM][t / T::FM], fb[cs][t / T::FM], fa[cs][t % T::FM]);
             if constexpr (RD)
                 if (t % RS == 0 && t / RS < R) read_one(1 - cs, ra_base, rb_base, t / RS);
             if constexpr (LD)
