@@ -4,10 +4,20 @@ One hipcc invocation compiles the HIP kernels and the C ABI ahead of time for
 gfx950 only.  ``-Xclang -target-feature -Xclang -packed-fp32-ops`` keeps the
 compiler from emitting packed fp32 arithmetic (v_pk_*_f32); the host pass
 warns that it does not know the feature, which is harmless.
+
+The same invocation asks the compiler for each kernel's resource usage
+(``-Rpass-analysis=kernel-resource-usage``: registers, scratch, spills,
+occupancy, LDS).  The build fails if any kernel in the library uses scratch
+memory or spills registers: a spill puts per-lane scratch traffic into the
+K loop and slows a kernel by tens of percent without changing its results,
+so nothing else would notice.  The table is written beside the library as
+``libgemm_nt_f16.resources.json``.
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -17,6 +27,7 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "gemm_nt_f16.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgemm_nt_f16.so")
+RESOURCES = os.path.join(HERE, "libgemm_nt_f16.resources.json")
 ARCH = "gfx950"
 
 
@@ -41,18 +52,66 @@ def flags():
     ]
 
 
+_FIELDS = {
+    "TotalSGPRs": "sgprs",
+    "VGPRs": "vgprs",
+    "AGPRs": "agprs",
+    "ScratchSize [bytes/lane]": "scratch_bytes_per_lane",
+    "Occupancy [waves/SIMD]": "waves_per_simd",
+    "SGPRs Spill": "sgpr_spill",
+    "VGPRs Spill": "vgpr_spill",
+    "LDS Size [bytes/block]": "lds_bytes",
+}
+
+
+def parse_resource_usage(stderr: str) -> dict:
+    """The compiler's kernel-resource-usage remarks -> {kernel symbol: {field: int}}."""
+    kernels, cur = {}, None
+    for line in stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+(.+?): (\S+) \[-Rpass-analysis=kernel-resource-usage\]", line)
+        if m and cur is not None and m.group(1).strip() in _FIELDS:
+            try:
+                cur[_FIELDS[m.group(1).strip()]] = int(m.group(2))
+            except ValueError:
+                pass
+    return kernels
+
+
+def spilling(kernels: dict) -> list:
+    """Kernels that use scratch memory or spill registers."""
+    return sorted(k for k, r in kernels.items()
+                  if r.get("scratch_bytes_per_lane", 0) or r.get("vgpr_spill", 0) or r.get("sgpr_spill", 0))
+
+
 def build(verbose: bool = False, extra=()) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *flags(), *extra, SRC, "-o", tmp]
+    cmd = [hipcc(), *flags(), "-Rpass-analysis=kernel-resource-usage", *extra, SRC, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "kernel-resource-usage")
+    err = "\n".join(l for l in res.stderr.splitlines()
+                    if not any(n in l for n in noise) and not re.match(r"^\s*(\d+ \||\|)", l))
     if res.returncode != 0:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
+    kernels = parse_resource_usage(res.stderr)
+    if not kernels:
+        os.remove(tmp)
+        raise RuntimeError("hipcc printed no kernel resource usage; cannot check for spills")
+    bad = spilling(kernels)
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError("kernels use scratch memory or spill registers:\n" +
+                           "\n".join("  %s: %s" % (k, kernels[k]) for k in bad))
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+    with open(RESOURCES + ".tmp", "w") as f:
+        json.dump({"arch": ARCH, "kernels": kernels}, f, indent=1, sort_keys=True)
+    os.replace(RESOURCES + ".tmp", RESOURCES)
     os.replace(tmp, LIB)
     return LIB
 

@@ -57,9 +57,8 @@
 // gemm_nt_f16_ordered (four or eight waves, K loop in a fixed hand-placed
 // order, one tile per workgroup), gemm_nt_f16_ordered_persist (its
 // persistent 5-slot form: the default for large shapes),
-// gemm_nt_f16_stream / _asm / _asm_split (32x32x16 persistent and
-// inline-assembly ablations), gemm_nt_f16_simple (one output per thread,
-// for K % 8 != 0 and unaligned operands).
+// gemm_nt_f16_simple (one output per thread, for K % 8 != 0 and unaligned
+// operands).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -1182,697 +1181,28 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
-// Persistent streaming variant of the kernel above.  The grid holds one
-// workgroup per compute unit; workgroup b computes tiles b, b + G, b + 2G, ...
-// (G = grid size) in the raster order of tile_coords.  The load cursor runs
-// through that tile sequence as one continuous stream of K steps: while the
-// last steps of a tile are computed, the first steps of the next tile are
-// already being loaded, so a tile change costs only the epilogue (no pipeline
-// drain and refill, no workgroup relaunch).  Past the last tile the cursor
-// reads from empty buffers, which return zeros into stages never read again.
-template <class T>
-__global__ void __launch_bounds__(T::THREADS, T::OCC)
-gemm_nt_f16_stream(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
-                   _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
-                   int group_m, int c_vec)
-{
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
-    const int total = tiles_m * tiles_n;
-    const int nk = (K + T::BK - 1) / T::BK;
-    const uint32_t row_bytes = (uint32_t)K * 2u;
-
-    const int fr_row = lane & 31;
-    const int fr_hi = lane >> 5;
-
-    float16_t acc[T::FM][T::FN];
-    auto zero_acc = [&]() {
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    };
-
-    if (nk == 0) {  // empty sum: every output is +0
-        zero_acc();
-        for (int t = blockIdx.x; t < total; t += gridDim.x) {
-            int tm, tn;
-            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
-            epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
-                        tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
-        }
-        return;
-    }
-
-    // Global->LDS copy assignment (independent of the tile): load j of this
-    // wave fills bytes [g * 1024, g * 1024 + 1024) of the operand's tile in
-    // the stage, g = wave * LOADS + j, i.e. ROWS_PER_LOAD whole rows; lane l
-    // writes position l % CHUNKS of row g * ROWS_PER_LOAD + l / CHUNKS, so it
-    // fetches the logical chunk that the swizzle puts at that position.
-    const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
-    uint32_t a_voff[T::A_LOADS], b_voff[T::B_LOADS];
-    int a_kc[T::A_LOADS], b_kc[T::B_LOADS];
-#pragma unroll
-    for (int j = 0; j < T::A_LOADS; ++j) {
-        const int row = (wave * T::A_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
-        const int c = swz<T>(row, ld_p);
-        a_voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
-        a_kc[j] = c * 8;
-    }
-#pragma unroll
-    for (int j = 0; j < T::B_LOADS; ++j) {
-        const int row = (wave * T::B_LOADS + j) * T::ROWS_PER_LOAD + ld_r;
-        const int c = swz<T>(row, ld_p);
-        b_voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
-        b_kc[j] = c * 8;
-    }
-
-    // Load cursor: tile ld_tile, step ld_ks; ld_ra / ld_rb cover that tile's
-    // rows (rows past M or N read as zero; past the last tile, everything).
-    int ld_tile = blockIdx.x, ld_ks = 0;
-    __amdgpu_buffer_rsrc_t ld_ra, ld_rb;
-    auto set_load_tile = [&](int t) {
-        if (t < total) {
-            int tm, tn;
-            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
-            const int m0 = tm * T::BM, n0 = tn * T::BN;
-            ld_ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(T::BM, M - m0) * row_bytes);
-            ld_rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)min(T::BN, N - n0) * row_bytes);
-        } else {
-            ld_ra = make_rsrc(A, 0u);
-            ld_rb = make_rsrc(B, 0u);
-        }
-    };
-    auto advance_cursor = [&]() {
-        if (++ld_ks == nk) {
-            ld_ks = 0;
-            ld_tile += gridDim.x;
-            set_load_tile(ld_tile);
-        }
-    };
-    // Loads of the cursor's step into `stage`.  K tail: chunks at or past K
-    // read as zero for both operands, so the padding adds nothing.
-    auto issue_loads = [&](int stage) {
-        const int k0 = ld_ks * T::BK;
-        const int krem = K - k0;
-        const uint32_t soff = (uint32_t)k0 * 2u;
-        unsigned char* a_dst = smem + stage * T::STAGE_BYTES + wave * T::A_LOADS * 1024;
-        unsigned char* b_dst = smem + stage * T::STAGE_BYTES + T::A_BYTES + wave * T::B_LOADS * 1024;
-#pragma unroll
-        for (int j = 0; j < T::A_LOADS; ++j) {
-            const uint32_t v = a_kc[j] < krem ? a_voff[j] : kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_ra, (lds_void_t*)(a_dst + j * 1024), 16, v, soff,
-                                                     0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < T::B_LOADS; ++j) {
-            const uint32_t v = b_kc[j] < krem ? b_voff[j] : kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_rb, (lds_void_t*)(b_dst + j * 1024), 16, v, soff,
-                                                     0, 0);
-        }
-    };
-
-    const int a_row0 = wm * T::WTM + fr_row;
-    const int b_row0 = wn * T::WTN + fr_row;
-    int fr_pos[T::KK];
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, 2 * kk + fr_hi) * 16;
-
-    half8_t fa[2][T::FM], fb[2][T::FN];
-    auto read_frags = [&](int buf, const unsigned char* stage_base, int kk) {
-        const unsigned char* pa = stage_base + a_row0 * T::ROW_BYTES + fr_pos[kk];
-        const unsigned char* pb = stage_base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[kk];
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i) fa[buf][i] = *(const half8_t*)(pa + i * 32 * T::ROW_BYTES);
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) fb[buf][j] = *(const half8_t*)(pb + j * 32 * T::ROW_BYTES);
-    };
-    auto mma = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[buf][j], fa[buf][i], acc[i][j],
-                                                                   0, 0, 0);
-    };
-
-    // Prologue: steps 0 .. STAGES-2 of the first tile, wait for step 0.
-    set_load_tile(ld_tile);
-#pragma unroll
-    for (int s = 0; s < T::STAGES - 1; ++s) {
-        issue_loads(s);
-        advance_cursor();
-    }
-    lds_barrier<T::LOADS * (T::STAGES - 2)>();
-    issue_loads(T::STAGES - 1);
-    advance_cursor();
-    read_frags(0, smem, 0);
-
-    int cur = 0;  // stage of the step being computed
-    for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        zero_acc();
-        for (int ks = 0; ks < nk; ++ks) {
-            const unsigned char* base = smem + cur * T::STAGE_BYTES;
-            const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
-#pragma unroll
-            for (int kk = 0; kk + 1 < T::KK; ++kk) {
-                read_frags((kk + 1) & 1, base, kk + 1);
-                mma(kk & 1);
-            }
-#pragma unroll
-            for (int kk = 0; kk + 1 < T::KK; ++kk) {
-                __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
-                __builtin_amdgcn_sched_group_barrier(0x008, T::FM * T::FN, 0);  // MFMAs
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // Loads of the next step have landed (only the STAGES - 2 steps
-            // after it may be outstanding; after an epilogue its stores are
-            // outstanding too, so wait for everything there).
-            if (T::STAGES == 2 || ks == 0)
-                lds_barrier<0>();
-            else
-                lds_barrier<T::LOADS * (T::STAGES - 2)>();
-            __builtin_amdgcn_sched_barrier(0);
-            read_frags(T::KK & 1, smem + nxt * T::STAGE_BYTES, 0);
-            issue_loads(cur);
-            mma((T::KK - 1) & 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
-#pragma unroll
-            for (int i = 0; i < T::FM * T::FN; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);          // one MFMA
-                if (i < T::LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // one load
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            advance_cursor();
-            cur = nxt;
-        }
-        int tm, tn;
-        tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
-        epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
-                    tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
-    }
-    // no global->LDS load may still be writing when the workgroup ends
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-}
-
-// ---------------------------------------------------------------------------
-// Hand-scheduled main loop for the 256 x 256 tile with 4 waves (each wave a
-// 128 x 128 sub-tile = 4 x 4 blocks of 32 x 32, 256 fp32 accumulators per
-// lane in AGPRs) and BK = 64 (four k sub-steps of 16).  The issue order of a
-// sub-step is fixed in inline assembly so the compiler cannot regroup it:
-// the 16 MFMAs of sub-step kk run back to back while the 8 fragment reads of
-// sub-step kk+1 are interleaved between the first 8 of them.  Operand
-// registers are still chosen by the compiler.  Fragment reads issued inside
-// these blocks are invisible to the compiler's wait-count tracking, so each
-// block that consumes them starts with its own s_waitcnt lgkmcnt(0).
-// ---------------------------------------------------------------------------
-#define GEMM_MF(c, b, a) "v_mfma_f32_32x32x16_f16 %[" c "], %[" b "], %[" a "], %[" c "]\n\t"
-#define GEMM_DR(d, p, off) "ds_read_b128 %[" d "], %[" p "] offset:" #off "\n\t"
-#define GEMM_ACC_OPS(acc)                                                                    \
-    [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c02] "+a"(acc[0][2]), [c03] "+a"(acc[0][3]), \
-    [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]), [c12] "+a"(acc[1][2]), [c13] "+a"(acc[1][3]), \
-    [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c22] "+a"(acc[2][2]), [c23] "+a"(acc[2][3]), \
-    [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]), [c32] "+a"(acc[3][2]), [c33] "+a"(acc[3][3])
-
-// acc[i][j] += B-fragment j * A-fragment i for all 16 blocks; reads the next
-// sub-step's fragments (A rows at pa + 4096 i, B rows at pb + 4096 j).
-// The block first waits for the fragment reads issued before it.
-__device__ __forceinline__ void substep_4x4(float16_t (&acc)[4][4], const half8_t (&ca)[4],
-                                            const half8_t (&cb)[4], half8_t (&na)[4],
-                                            half8_t (&nb)[4], uint32_t pa, uint32_t pb)
-{
-    asm volatile(
-        "s_waitcnt lgkmcnt(0)\n\t"
-        GEMM_MF("c00", "b0", "a0") GEMM_DR("na0", "pa", 0)
-        GEMM_MF("c01", "b1", "a0") GEMM_DR("na1", "pa", 4096)
-        GEMM_MF("c02", "b2", "a0") GEMM_DR("na2", "pa", 8192)
-        GEMM_MF("c03", "b3", "a0") GEMM_DR("na3", "pa", 12288)
-        GEMM_MF("c10", "b0", "a1") GEMM_DR("nb0", "pb", 0)
-        GEMM_MF("c11", "b1", "a1") GEMM_DR("nb1", "pb", 4096)
-        GEMM_MF("c12", "b2", "a1") GEMM_DR("nb2", "pb", 8192)
-        GEMM_MF("c13", "b3", "a1") GEMM_DR("nb3", "pb", 12288)
-        GEMM_MF("c20", "b0", "a2") GEMM_MF("c21", "b1", "a2")
-        GEMM_MF("c22", "b2", "a2") GEMM_MF("c23", "b3", "a2")
-        GEMM_MF("c30", "b0", "a3") GEMM_MF("c31", "b1", "a3")
-        GEMM_MF("c32", "b2", "a3") GEMM_MF("c33", "b3", "a3")
-        : GEMM_ACC_OPS(acc),
-          [na0] "=&v"(na[0]), [na1] "=&v"(na[1]), [na2] "=&v"(na[2]), [na3] "=&v"(na[3]),
-          [nb0] "=&v"(nb[0]), [nb1] "=&v"(nb[1]), [nb2] "=&v"(nb[2]), [nb3] "=&v"(nb[3])
-        : [a0] "v"(ca[0]), [a1] "v"(ca[1]), [a2] "v"(ca[2]), [a3] "v"(ca[3]),
-          [b0] "v"(cb[0]), [b1] "v"(cb[1]), [b2] "v"(cb[2]), [b3] "v"(cb[3]),
-          [pa] "v"(pa), [pb] "v"(pb)
-        : "memory");
-}
-
-// The four MFMAs of block row i (acc[i][0..3]), no fragment reads.
-template <int I>
-__device__ __forceinline__ void mfma_row_4(float16_t (&acc)[4][4], const half8_t& ca,
-                                           const half8_t (&cb)[4])
-{
-    asm volatile(
-        "v_mfma_f32_32x32x16_f16 %[c0], %[b0], %[a], %[c0]\n\t"
-        "v_mfma_f32_32x32x16_f16 %[c1], %[b1], %[a], %[c1]\n\t"
-        "v_mfma_f32_32x32x16_f16 %[c2], %[b2], %[a], %[c2]\n\t"
-        "v_mfma_f32_32x32x16_f16 %[c3], %[b3], %[a], %[c3]\n\t"
-        : [c0] "+a"(acc[I][0]), [c1] "+a"(acc[I][1]), [c2] "+a"(acc[I][2]), [c3] "+a"(acc[I][3])
-        : [a] "v"(ca), [b0] "v"(cb[0]), [b1] "v"(cb[1]), [b2] "v"(cb[2]), [b3] "v"(cb[3])
-        : "memory");
-}
-
-// Eight fragment reads (A rows at pa + 4096 i, B rows at pb + 4096 j).
-__device__ __forceinline__ void read_frags_4x4(half8_t (&na)[4], half8_t (&nb)[4], uint32_t pa,
-                                               uint32_t pb)
-{
-    asm volatile(
-        GEMM_DR("na0", "pa", 0) GEMM_DR("na1", "pa", 4096) GEMM_DR("na2", "pa", 8192)
-        GEMM_DR("na3", "pa", 12288) GEMM_DR("nb0", "pb", 0) GEMM_DR("nb1", "pb", 4096)
-        GEMM_DR("nb2", "pb", 8192) GEMM_DR("nb3", "pb", 12288)
-        : [na0] "=&v"(na[0]), [na1] "=&v"(na[1]), [na2] "=&v"(na[2]), [na3] "=&v"(na[3]),
-          [nb0] "=&v"(nb[0]), [nb1] "=&v"(nb[1]), [nb2] "=&v"(nb[2]), [nb3] "=&v"(nb[3])
-        : [pa] "v"(pa), [pb] "v"(pb)
-        : "memory");
-}
-
-// Persistent streaming kernel with the hand-scheduled 4 x 4 main loop
-// (the same tile order, load cursor, LDS layout, K-tail handling and
-// epilogue as gemm_nt_f16_stream).  Per K step (stage p):
-//   three blocks: MFMAs of sub-steps 0, 1, 2, each with the next
-//     sub-step's fragment reads interleaved;
-//   s_waitcnt vmcnt(0) lgkmcnt(0); s_barrier: the next step's stage is
-//     loaded and visible, and every wave is done reading stage p;
-//   the MFMAs of sub-step 3 in four rows of four, the first row with the
-//     next step's sub-step-0 reads interleaved, each row followed by four
-//     global->LDS loads of step + 2 into stage p.
-template <class T>
-__global__ void __launch_bounds__(T::THREADS, T::OCC)
-gemm_nt_f16_asm(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
-                _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
-                int group_m, int c_vec)
-{
-    static_assert(T::FM == 4 && T::FN == 4 && T::KK == 4 && T::STAGES == 2 && T::LOADS == 16,
-                  "the hand-scheduled loop is written for 4 x 4 blocks, BK = 64, 2 stages");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
-    const int total = tiles_m * tiles_n;
-    const int nk = (K + T::BK - 1) / T::BK;
-    const uint32_t row_bytes = (uint32_t)K * 2u;
-
-    const int fr_row = lane & 31;
-    const int fr_hi = lane >> 5;
-
-    float16_t acc[4][4];
-    auto zero_acc = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-        // accumulator writes must settle before an MFMA reads them
-        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-    };
-    auto finish_mfma = [&]() {
-        // the last MFMAs' results must be written before they are read
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    };
-
-    if (nk == 0) {  // empty sum: every output is +0
-        zero_acc();
-        for (int t = blockIdx.x; t < total; t += gridDim.x) {
-            int tm, tn;
-            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
-            epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
-                        tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
-        }
-        return;
-    }
-
-    const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
-    uint32_t voff[T::LOADS];
-    int kc[T::LOADS];
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) {
-        const bool is_a = j < T::A_LOADS;
-        const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
-        const int row = g * T::ROWS_PER_LOAD + ld_r;
-        const int c = swz<T>(row, ld_p);
-        voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
-        kc[j] = c * 8;
-    }
-
-    int ld_tile = blockIdx.x, ld_ks = 0;
-    __amdgpu_buffer_rsrc_t ld_ra, ld_rb;
-    auto set_load_tile = [&](int t) {
-        if (t < total) {
-            int tm, tn;
-            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
-            const int m0 = tm * T::BM, n0 = tn * T::BN;
-            ld_ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(T::BM, M - m0) * row_bytes);
-            ld_rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)min(T::BN, N - n0) * row_bytes);
-        } else {
-            ld_ra = make_rsrc(A, 0u);
-            ld_rb = make_rsrc(B, 0u);
-        }
-    };
-    auto advance_cursor = [&]() {
-        if (++ld_ks == nk) {
-            ld_ks = 0;
-            ld_tile += gridDim.x;
-            set_load_tile(ld_tile);
-        }
-    };
-    // loads j0 .. j0+3 of the cursor's step into `stage`
-    auto issue_loads4 = [&](int stage, int j0) {
-        const int k0 = ld_ks * T::BK;
-        const int krem = K - k0;
-        const uint32_t soff = (uint32_t)k0 * 2u;
-#pragma unroll
-        for (int j = j0; j < j0 + 4; ++j) {
-            const bool is_a = j < T::A_LOADS;
-            const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
-            unsigned char* dst = smem + stage * T::STAGE_BYTES + (is_a ? 0 : T::A_BYTES) + g * 1024;
-            const uint32_t v = kc[j] < krem ? voff[j] : kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ld_ra : ld_rb, (lds_void_t*)dst, 16, v,
-                                                     soff, 0, 0);
-        }
-    };
-
-    // LDS byte address of this lane's fragment row, per operand and sub-step
-    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-    const uint32_t a_row_off = (uint32_t)((wm * T::WTM + fr_row) * T::ROW_BYTES);
-    const uint32_t b_row_off = (uint32_t)(T::A_BYTES + (wn * T::WTN + fr_row) * T::ROW_BYTES);
-    uint32_t fr_pos[T::KK];
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = (uint32_t)swz<T>(fr_row, 2 * kk + fr_hi) * 16u;
-
-    half8_t fa0[4], fb0[4], fa1[4], fb1[4];
-
-    set_load_tile(ld_tile);
-    issue_loads4(0, 0);
-    issue_loads4(0, 4);
-    issue_loads4(0, 8);
-    issue_loads4(0, 12);
-    advance_cursor();
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    issue_loads4(1, 0);
-    issue_loads4(1, 4);
-    issue_loads4(1, 8);
-    issue_loads4(1, 12);
-    advance_cursor();
-    read_frags_4x4(fa0, fb0, smem_base + a_row_off + fr_pos[0], smem_base + b_row_off + fr_pos[0]);
-
-    uint32_t cur = 0;  // stage of the step being computed
-    for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        zero_acc();
-        for (int ks = 0; ks < nk; ++ks) {
-            const uint32_t sb = smem_base + cur * T::STAGE_BYTES;
-            const uint32_t nb = smem_base + (cur ^ 1u) * T::STAGE_BYTES;
-            substep_4x4(acc, fa0, fb0, fa1, fb1, sb + a_row_off + fr_pos[1], sb + b_row_off + fr_pos[1]);
-            substep_4x4(acc, fa1, fb1, fa0, fb0, sb + a_row_off + fr_pos[2], sb + b_row_off + fr_pos[2]);
-            substep_4x4(acc, fa0, fb0, fa1, fb1, sb + a_row_off + fr_pos[3], sb + b_row_off + fr_pos[3]);
-            // next step's stage landed (own loads) and visible (barrier);
-            // everyone is done with stage `cur`
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            read_frags_4x4(fa0, fb0, nb + a_row_off + fr_pos[0], nb + b_row_off + fr_pos[0]);
-            mfma_row_4<0>(acc, fa1[0], fb1);
-            issue_loads4((int)cur, 0);
-            mfma_row_4<1>(acc, fa1[1], fb1);
-            issue_loads4((int)cur, 4);
-            mfma_row_4<2>(acc, fa1[2], fb1);
-            issue_loads4((int)cur, 8);
-            mfma_row_4<3>(acc, fa1[3], fb1);
-            issue_loads4((int)cur, 12);
-            advance_cursor();
-            cur ^= 1u;
-        }
-        finish_mfma();
-        int tm, tn;
-        tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
-        epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
-                    tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
-    }
-    // no global->LDS load or fragment read may still be in flight at the end
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-}
-
-// ---------------------------------------------------------------------------
-// Split-load hand-scheduled kernel (4 x 4 blocks per wave, any BK and
-// STAGES).  A sub-step's 16 MFMAs are issued as four rows of four; the first row
-// carries the 8 fragment reads of the next sub-step, and one global->LDS
-// load goes between consecutive rows.  The loads of step s are split: the
-// first four are issued right after the barrier that frees their stage
-// (after step s - STAGES), the rest between the rows of the following
-// step's first sub-steps.  Every load thus has STAGES - 2 full steps to
-// arrive, and the texture path sees a steady trickle instead of a burst.
-// ---------------------------------------------------------------------------
-// Row I of 4 MFMAs (acc[I][j] += B-frag j * A-frag), optionally waiting for
-// earlier fragment reads first and optionally reading the next sub-step's
-// fragments (A rows at pa + i * STRIDE, B rows at pb + j * STRIDE).
-template <int I, bool WAIT, int STRIDE>
-__device__ __forceinline__ void mma_row_reads(float16_t (&acc)[4][4], const half8_t& ca,
-                                              const half8_t (&cb)[4], half8_t (&na)[4],
-                                              half8_t (&nb)[4], uint32_t pa, uint32_t pb)
-{
-    if (WAIT) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    asm volatile(
-        "v_mfma_f32_32x32x16_f16 %[c0], %[b0], %[a], %[c0]\n\t"
-        "ds_read_b128 %[na0], %[pa] offset:0\n\t"
-        "ds_read_b128 %[na1], %[pa] offset:%[s1]\n\t"
-        "v_mfma_f32_32x32x16_f16 %[c1], %[b1], %[a], %[c1]\n\t"
-        "ds_read_b128 %[na2], %[pa] offset:%[s2]\n\t"
-        "ds_read_b128 %[na3], %[pa] offset:%[s3]\n\t"
-        "v_mfma_f32_32x32x16_f16 %[c2], %[b2], %[a], %[c2]\n\t"
-        "ds_read_b128 %[nb0], %[pb] offset:0\n\t"
-        "ds_read_b128 %[nb1], %[pb] offset:%[s1]\n\t"
-        "v_mfma_f32_32x32x16_f16 %[c3], %[b3], %[a], %[c3]\n\t"
-        "ds_read_b128 %[nb2], %[pb] offset:%[s2]\n\t"
-        "ds_read_b128 %[nb3], %[pb] offset:%[s3]\n\t"
-        : [c0] "+a"(acc[I][0]), [c1] "+a"(acc[I][1]), [c2] "+a"(acc[I][2]), [c3] "+a"(acc[I][3]),
-          [na0] "=&v"(na[0]), [na1] "=&v"(na[1]), [na2] "=&v"(na[2]), [na3] "=&v"(na[3]),
-          [nb0] "=&v"(nb[0]), [nb1] "=&v"(nb[1]), [nb2] "=&v"(nb[2]), [nb3] "=&v"(nb[3])
-        : [a] "v"(ca), [b0] "v"(cb[0]), [b1] "v"(cb[1]), [b2] "v"(cb[2]), [b3] "v"(cb[3]),
-          [pa] "v"(pa), [pb] "v"(pb), [s1] "i"(STRIDE), [s2] "i"(2 * STRIDE), [s3] "i"(3 * STRIDE)
-        : "memory");
-}
-
-template <int BM_, int BN_, int BK_, int STAGES_>
-using Asm4x4 = TileShape<BM_, BN_, BK_, 2, 2, STAGES_, 1>;
-
-template <class T>
-__global__ void __launch_bounds__(T::THREADS, T::OCC)
-gemm_nt_f16_asm_split(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
-                      _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
-                      int group_m, int c_vec)
-{
-    static_assert(T::FM == 4 && T::FN == 4 && T::WAVES == 4, "4 waves of 4 x 4 blocks");
-    static_assert(T::STAGES >= 2, "a two-stage ring at least");
-    constexpr int L = T::LOADS;              // global->LDS loads per wave per step
-    constexpr int FIRST = 4;                 // issued right after the barrier
-    constexpr int REST = L - FIRST;          // issued during the next step's sub-steps
-    constexpr int GAPS = (T::KK - 1) * 4;    // row gaps before the barrier
-    static_assert(REST <= GAPS, "every remaining load needs a row gap");
-    constexpr int WAIT_VM = (T::STAGES - 2) * L;
-    static_assert(WAIT_VM <= 63 && WAIT_VM + FIRST <= 63, "vmcnt holds at most 63");
-    constexpr int STRIDE = 32 * T::ROW_BYTES;  // bytes between 32-row fragment blocks
-
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
-    const int total = tiles_m * tiles_n;
-    const int nk = (K + T::BK - 1) / T::BK;
-    const uint32_t row_bytes = (uint32_t)K * 2u;
-    const int fr_row = lane & 31;
-    const int fr_hi = lane >> 5;
-
-    float16_t acc[4][4];
-    auto zero_acc = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-    };
-
-    if (nk == 0) {  // empty sum: every output is +0
-        zero_acc();
-        for (int t = blockIdx.x; t < total; t += gridDim.x) {
-            int tm, tn;
-            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
-            epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
-                        tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
-        }
-        return;
-    }
-
-    const int ld_r = lane / T::CHUNKS, ld_p = lane % T::CHUNKS;
-    uint32_t voff[L];
-    int kc[L];
-#pragma unroll
-    for (int j = 0; j < L; ++j) {
-        const bool is_a = j < T::A_LOADS;
-        const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
-        const int row = g * T::ROWS_PER_LOAD + ld_r;
-        const int c = swz<T>(row, ld_p);
-        voff[j] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
-        kc[j] = c * 8;
-    }
-
-    int ld_tile = blockIdx.x, ld_ks = 0, ld_stage = 0;
-    __amdgpu_buffer_rsrc_t ld_ra, ld_rb;
-    auto set_load_tile = [&](int t) {
-        if (t < total) {
-            int tm, tn;
-            tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
-            const int m0 = tm * T::BM, n0 = tn * T::BN;
-            ld_ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(T::BM, M - m0) * row_bytes);
-            ld_rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)min(T::BN, N - n0) * row_bytes);
-        } else {
-            ld_ra = make_rsrc(A, 0u);
-            ld_rb = make_rsrc(B, 0u);
-        }
-    };
-    auto advance_cursor = [&]() {
-        ld_stage = ld_stage + 1 == T::STAGES ? 0 : ld_stage + 1;
-        if (++ld_ks == nk) {
-            ld_ks = 0;
-            ld_tile += gridDim.x;
-            set_load_tile(ld_tile);
-        }
-    };
-    // load j of the cursor's step into the cursor's stage
-    auto load_one = [&](int j) {
-        const int k0 = ld_ks * T::BK;
-        const bool is_a = j < T::A_LOADS;
-        const int g = wave * (is_a ? T::A_LOADS : T::B_LOADS) + (is_a ? j : j - T::A_LOADS);
-        unsigned char* dst = smem + ld_stage * T::STAGE_BYTES + (is_a ? 0 : T::A_BYTES) + g * 1024;
-        const uint32_t v = kc[j] < K - k0 ? voff[j] : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ld_ra : ld_rb, (lds_void_t*)dst, 16, v,
-                                                 (uint32_t)k0 * 2u, 0, 0);
-    };
-
-    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-    const uint32_t a_row_off = (uint32_t)((wm * T::WTM + fr_row) * T::ROW_BYTES);
-    const uint32_t b_row_off = (uint32_t)(T::A_BYTES + (wn * T::WTN + fr_row) * T::ROW_BYTES);
-    uint32_t fr_pos[T::KK];
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = (uint32_t)swz<T>(fr_row, 2 * kk + fr_hi) * 16u;
-
-    half8_t fa[2][4], fb[2][4];
-
-    // Prologue: steps 0 .. STAGES-2 whole, the first loads of step STAGES-1.
-    set_load_tile(ld_tile);
-    for (int s = 0; s < T::STAGES - 1; ++s) {
-#pragma unroll
-        for (int j = 0; j < L; ++j) load_one(j);
-        advance_cursor();
-    }
-#pragma unroll
-    for (int j = 0; j < FIRST; ++j) load_one(j);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_VM + FIRST));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // fragments of step 0, sub-step 0
-    asm volatile(
-        "ds_read_b128 %[a0], %[pa] offset:0\n\tds_read_b128 %[a1], %[pa] offset:%[s1]\n\t"
-        "ds_read_b128 %[a2], %[pa] offset:%[s2]\n\tds_read_b128 %[a3], %[pa] offset:%[s3]\n\t"
-        "ds_read_b128 %[b0], %[pb] offset:0\n\tds_read_b128 %[b1], %[pb] offset:%[s1]\n\t"
-        "ds_read_b128 %[b2], %[pb] offset:%[s2]\n\tds_read_b128 %[b3], %[pb] offset:%[s3]\n\t"
-        : [a0] "=&v"(fa[0][0]), [a1] "=&v"(fa[0][1]), [a2] "=&v"(fa[0][2]), [a3] "=&v"(fa[0][3]),
-          [b0] "=&v"(fb[0][0]), [b1] "=&v"(fb[0][1]), [b2] "=&v"(fb[0][2]), [b3] "=&v"(fb[0][3])
-        : [pa] "v"(smem_base + a_row_off + fr_pos[0]), [pb] "v"(smem_base + b_row_off + fr_pos[0]),
-          [s1] "i"(STRIDE), [s2] "i"(2 * STRIDE), [s3] "i"(3 * STRIDE)
-        : "memory");
-
-    int cur = 0;  // stage of the step being computed
-    bool after_epilogue = false;
-    for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        zero_acc();
-        for (int ks = 0; ks < nk; ++ks) {
-            const uint32_t sb = smem_base + (uint32_t)(cur * T::STAGE_BYTES);
-            const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
-            const uint32_t nb = smem_base + (uint32_t)(nxt * T::STAGE_BYTES);
-            // sub-steps 0 .. KK-2; the remaining loads of the cursor's step
-            // go into the row gaps
-#pragma unroll
-            for (int kk = 0; kk + 1 < T::KK; ++kk) {
-                const int cb_ = kk & 1, nb_ = (kk + 1) & 1;
-                const uint32_t pa = sb + a_row_off + fr_pos[kk + 1];
-                const uint32_t pb = sb + b_row_off + fr_pos[kk + 1];
-                mma_row_reads<0, true, STRIDE>(acc, fa[cb_][0], fb[cb_], fa[nb_], fb[nb_], pa, pb);
-                if (kk * 4 + 0 < REST) load_one(FIRST + kk * 4 + 0);
-                mfma_row_4<1>(acc, fa[cb_][1], fb[cb_]);
-                if (kk * 4 + 1 < REST) load_one(FIRST + kk * 4 + 1);
-                mfma_row_4<2>(acc, fa[cb_][2], fb[cb_]);
-                if (kk * 4 + 2 < REST) load_one(FIRST + kk * 4 + 2);
-                mfma_row_4<3>(acc, fa[cb_][3], fb[cb_]);
-                if (kk * 4 + 3 < REST) load_one(FIRST + kk * 4 + 3);
-            }
-            advance_cursor();
-            // step ks + 1 has landed and is visible; stage `cur` is free.
-            // After an epilogue its stores are outstanding too: wait for all.
-            if (after_epilogue)
-                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(%[n]) lgkmcnt(0)\n\ts_barrier" ::
-                                 [n] "i"(WAIT_VM) : "memory");
-            after_epilogue = false;
-            // last sub-step, with the next step's first fragments and the
-            // first loads of the cursor's step (into stage `cur`)
-            {
-                constexpr int cb_ = (T::KK - 1) & 1;
-                const uint32_t pa = nb + a_row_off + fr_pos[0];
-                const uint32_t pb = nb + b_row_off + fr_pos[0];
-                mma_row_reads<0, false, STRIDE>(acc, fa[cb_][0], fb[cb_], fa[0], fb[0], pa, pb);
-                load_one(0);
-                mfma_row_4<1>(acc, fa[cb_][1], fb[cb_]);
-                load_one(1);
-                mfma_row_4<2>(acc, fa[cb_][2], fb[cb_]);
-                load_one(2);
-                mfma_row_4<3>(acc, fa[cb_][3], fb[cb_]);
-                load_one(3);
-            }
-            cur = nxt;
-        }
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-        int tm, tn;
-        tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
-        epilogue<T>(acc, C, M, N, tm * T::BM + wm * T::WTM + fr_row,
-                    tn * T::BN + wn * T::WTN + 4 * fr_hi, c_vec);
-        after_epilogue = true;
-    }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-}
-
 // Plain per-element kernel for inputs the MFMA kernels do not take
 // (unaligned pointers, K % 8 != 0, very long K).  One thread per output,
-// fp32 accumulation in k order, one fp16 rounding at the end.
+// fp32 accumulation in k order, one fp16 rounding at the end.  The grid is
+// one-dimensional and at most kSimpleGrid workgroups of 16 x 16 outputs;
+// workgroup g covers blocks g, g + gridDim.x, ... of the row-major order of
+// 16 x 16 blocks of C, so every M, N < 2^31 runs.
 __global__ void __launch_bounds__(256)
 gemm_nt_f16_simple(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                    _Float16* __restrict__ C, int64_t M, int64_t N, int64_t K)
 {
-    const int64_t n = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
-    const int64_t m = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
-    if (m >= M || n >= N) return;
-    const _Float16* a = A + m * K;
-    const _Float16* b = B + n * K;
-    float s = 0.0f;
-    for (int64_t k = 0; k < K; ++k) s += (float)a[k] * (float)b[k];
-    C[m * N + n] = (_Float16)s;
+    const int64_t blocks_n = (N + 15) / 16;
+    const int64_t blocks = ((M + 15) / 16) * blocks_n;
+    for (int64_t blk = blockIdx.x; blk < blocks; blk += gridDim.x) {
+        const int64_t m = (blk / blocks_n) * 16 + (threadIdx.x >> 4);
+        const int64_t n = (blk % blocks_n) * 16 + (threadIdx.x & 15);
+        if (m >= M || n >= N) continue;
+        const _Float16* a = A + m * K;
+        const _Float16* b = B + n * K;
+        float s = 0.0f;
+        for (int64_t k = 0; k < K; ++k) s += (float)a[k] * (float)b[k];
+        C[m * N + n] = (_Float16)s;
+    }
 }
 
 // ------------------------------------------------------------------ host --
@@ -1979,65 +1309,14 @@ int num_cus(int device)
     return n;
 }
 
-template <class T>
-int launch_asm_split(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                     int group_m, hipStream_t stream)
-{
-    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
-    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
-    int device = 0;
-    if (hipGetDevice(&device) != hipSuccess) device = 0;
-    const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus(device));
-    const int c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
-    hipLaunchKernelGGL((gemm_nt_f16_asm_split<T>), dim3((unsigned)grid), dim3(T::THREADS), 0,
-                       stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M,
-                       (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
-    return (int)hipGetLastError();
-}
-
-template <class T, bool ASM>
-int launch_persistent(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                      int group_m, hipStream_t stream)
-{
-    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
-    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
-    int device = 0;
-    if (hipGetDevice(&device) != hipSuccess) device = 0;
-    const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus(device));
-    const int c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
-    if (ASM)
-        hipLaunchKernelGGL((gemm_nt_f16_asm<T>), dim3((unsigned)grid), dim3(T::THREADS), 0, stream,
-                           (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N,
-                           (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
-    else
-        hipLaunchKernelGGL((gemm_nt_f16_stream<T>), dim3((unsigned)grid), dim3(T::THREADS), 0,
-                           stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M,
-                           (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
-    return (int)hipGetLastError();
-}
-
-template <class T>
-int launch_stream(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                  int group_m, hipStream_t stream)
-{
-    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
-    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
-    int device = 0;
-    if (hipGetDevice(&device) != hipSuccess) device = 0;
-    const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus(device));
-    const int c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
-    hipLaunchKernelGGL((gemm_nt_f16_stream<T>), dim3((unsigned)grid), dim3(T::THREADS), 0, stream,
-                       (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N,
-                       (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
-    return (int)hipGetLastError();
-}
+constexpr int64_t kSimpleGrid = int64_t(1) << 20;  // workgroups of the per-element kernel at most
 
 int launch_simple(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int,
                   hipStream_t stream)
 {
-    const int64_t gx = (N + 15) / 16, gy = (M + 15) / 16;
-    if (gx > kMaxMN || gy > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(gemm_nt_f16_simple, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream,
+    const int64_t blocks = ((M + 15) / 16) * ((N + 15) / 16);  // < 2^54 for M, N < 2^31
+    const int64_t grid = std::min(blocks, kSimpleGrid);
+    hipLaunchKernelGGL(gemm_nt_f16_simple, dim3((unsigned)grid), dim3(256), 0, stream,
                        (const _Float16*)A, (const _Float16*)B, (_Float16*)C, M, N, K);
     return (int)hipGetLastError();
 }
@@ -2073,9 +1352,6 @@ constexpr Variant kVariants[] = {
     {"mfma32_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4>},
     {"mfma32_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4>},
     {"mfma32_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4>},
-    {"mfma32_256x256x64_w4_stream", 256, 256, 8, launch_stream<T256_k64_s2_w4>},
-    {"mfma32_256x256x64_w4_asm", 256, 256, 8, launch_persistent<T256_k64_s2_w4, true>},
-    {"mfma32_256x256x32_w4_s5_split", 256, 256, 8, launch_asm_split<Asm4x4<256, 256, 32, 5>>},
     {"simple_f32_per_element", 0, 0, 0, launch_simple},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

@@ -68,9 +68,6 @@ RUNGS = {
     "mfma16_128x128x64_w8_s3": "16x16x32 MFMAs, 128x128 tile, 8 waves",
     "mfma16_128x128x64_w8_s3_l4_ordered": "128x128 tile, 8 waves, 4 loading, issue order fixed by hand (default for mid sizes)",
     "mfma16_64x64x64_w4_s3": "16x16x32 MFMAs, 64x64 tile (default for small sizes)",
-    "mfma32_256x256x64_w4_stream": "persistent grid: the ring runs on across tile boundaries",
-    "mfma32_256x256x64_w4_asm": "persistent grid with a hand-scheduled (inline asm) main loop",
-    "mfma32_256x256x32_w4_s5_split": "hand-scheduled, loads split between MFMA rows, 5-stage BK-32 ring",
 }
 
 

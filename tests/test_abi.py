@@ -198,3 +198,50 @@ def test_launch_plan(lib):
         assert v == binding.gemm_nt_f16_select(*shape)
     assert plan(64, 64, 7) == (binding.gemm_nt_f16_select(64, 64, 7), 64, -1)
     assert plan(-1, 4, 4)[0] == -1
+
+
+def test_no_kernel_uses_scratch_or_spills(lib):
+    """The build records every kernel's resource usage (the compiler's
+    kernel-resource-usage remarks) beside the library and refuses to
+    produce a library in which any kernel spills; check the record of the
+    library that is loaded: every kernel present, none with scratch."""
+    import json
+
+    from dense_fp16_gemm_04_amd import build
+
+    if not os.path.exists(build.RESOURCES):
+        build.build()
+    with open(build.RESOURCES) as f:
+        kernels = json.load(f)["kernels"]
+    # one kernel per variant at most (some variants share one)
+    assert 0 < len(kernels) <= lib.gemm_nt_f16_variant_count()
+    assert build.spilling(kernels) == []
+    for name, r in kernels.items():
+        assert r["scratch_bytes_per_lane"] == 0 and r["vgpr_spill"] == 0 and r["sgpr_spill"] == 0, name
+        assert r["vgprs"] + r["agprs"] <= 512 and r["lds_bytes"] <= 160 * 1024, name
+    persist = [k for k in kernels if "ordered_persist" in k]
+    assert persist and all(kernels[k]["waves_per_simd"] >= 2 for k in persist)
+
+
+def test_spill_gate_flags_a_spilling_kernel():
+    """The gate's parser on remarks in the compiler's format, one kernel
+    clean and one with scratch and spilled registers."""
+    from dense_fp16_gemm_04_amd import build
+
+    text = "\n".join([
+        "k.hip:10:1: remark: Function Name: clean_kernel [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:10:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:10:1: remark:     AGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:10:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:10:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "   10 | {",
+        "k.hip:20:1: remark: Function Name: spilling_kernel [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:20:1: remark:     VGPRs: 256 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:20:1: remark:     ScratchSize [bytes/lane]: 44 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:20:1: remark:     VGPRs Spill: 10 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:20:1: remark:     Occupancy [waves/SIMD]: 1 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    k = build.parse_resource_usage(text)
+    assert k["clean_kernel"]["vgprs"] == 128 and k["clean_kernel"]["scratch_bytes_per_lane"] == 0
+    assert k["spilling_kernel"]["scratch_bytes_per_lane"] == 44 and k["spilling_kernel"]["waves_per_simd"] == 1
+    assert build.spilling(k) == ["spilling_kernel"]

@@ -9,7 +9,10 @@ The kernels address their operand tiles and C through 32-bit buffer offsets:
   then spans at most 2^31 bytes), through 64-bit pointer stores beyond, and
   the persistent kernel hands such products to its one-tile form;
 * from K = 2^22 the per-element kernel takes the product, and forcing an
-  MFMA kernel there is an error.
+  MFMA kernel there is an error;
+* the per-element kernel (K % 8 != 0, unaligned operands, K >= 2^22) walks
+  a one-dimensional grid over 16 x 16 blocks of C, so M may exceed the
+  65535 x 16 rows a two-dimensional grid would reach.
 
 Each case runs the library's own plan and each kernel the plan can choose,
 on integer inputs in {-1, 0, 1}: every partial sum is an integer below
@@ -96,3 +99,11 @@ def test_k_at_the_limit_takes_the_per_element_kernel():
         with pytest.raises(binding.GemmError):
             binding.gemm_nt_f16_ex(ta, tb, variant=ids[name])
     torch.cuda.synchronize()
+
+
+def test_per_element_kernel_past_65535_row_blocks():
+    """M = 1,048,577 rows with K = 7 (K % 8 != 0: only the per-element kernel
+    takes it): more blocks of 16 rows than a grid dimension of 65535 holds,
+    so the kernel's grid-stride loop must reach them, and the last block
+    holds a single row."""
+    check(ints(1048577, 7, 79), ints(3, 7, 80), "many-rows", names=["simple_f32_per_element"])
