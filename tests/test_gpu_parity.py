@@ -23,6 +23,7 @@ import functools
 import numpy as np
 import pytest
 
+import _errstats
 import oracle
 from dense_fp16_gemm_04_amd import binding, workloads
 
@@ -107,8 +108,8 @@ def test_workload_full_parity(name):
     print("case", name, binding.gemm_nt_f16_config_name(w.M, w.N, w.K), flush=True)
     got = run(a, b)
     c64, c16 = workload_oracle(name)
-    err = assert_close(got, c64, c16, w.K, name)
-    print("%s: max %.3g mean %.3g" % (name, err.max(), err.mean()))
+    assert_close(got, c64, c16, w.K, name)
+    _errstats.record(name, got, c64, c16, w.K)
 
 
 @pytest.mark.parametrize("M,N,K", [(2048, 2048, 2048), (256, 8192, 4096), (4352, 4352, 2048)])
@@ -126,30 +127,28 @@ def test_plan_shapes_gaussian(M, N, K):
     print("max %.3g mean %.3g" % (err.max(), err.mean()))
 
 
-def test_headline_sampled_parity_and_error_figures():
-    """M = N = K = 8192 in the launch configuration the benchmark times.
+def test_headline_full_parity_and_error_figures():
+    """M = N = K = 8192 through gemm_nt_f16, the launch the benchmark times,
+    compared with the oracle on all 67,108,864 outputs.
 
-    The oracle evaluates a sample of outputs one by one: whole first and last
-    rows and columns (tile edges), and 65536 random positions.  The error of
-    those outputs is compared with the pages' fp32-accumulation figures
-    (mean 0.00014, max 0.0020 at K = 8192).
+    Beyond the bar of every workload, the error distribution must be the
+    fp16 rounding of the exact result and nothing more: the pages report
+    mean 0.00014 and max 0.0020 for their fp32-accumulating kernel at this K
+    against an fp32 reference ("6. Four Consumers, FP16 Accumulation, and a
+    TMA Epilogue", "The Register Budget Problem"); half an fp16 ulp in the
+    [4, 8) binade is 0.00195, and a round-to-nearest cast has no bias.
     """
     name = "square_8192"
     w, a, b = workload_data(name)
     print("case", name, binding.gemm_nt_f16_config_name(w.M, w.N, w.K), flush=True)
     got = run(a, b)
-    g = np.random.Generator(np.random.PCG64(123))
-    rows = np.concatenate([np.zeros(w.N, np.int64), np.full(w.N, w.M - 1), np.arange(w.M),
-                           np.arange(w.M), g.integers(0, w.M, 65536)])
-    cols = np.concatenate([np.arange(w.N), np.arange(w.N), np.zeros(w.M, np.int64),
-                           np.full(w.M, w.N - 1), g.integers(0, w.N, 65536)])
-    c64 = oracle.gemm_nt_entries(a, b, rows, cols)
-    c16 = oracle.encode_rne(c64).view(np.float16)
-    err = assert_close(got[rows, cols], c64, c16, w.K, name)
-    assert abs(err.mean() - 1.4e-4) < 0.3e-4, err.mean()
-    assert err.max() <= 2.0e-3 + 1e-5
-    signed = (got[rows, cols].astype(np.float64) - c64).mean()
-    assert abs(signed) < 2e-5  # round to nearest: no bias toward zero
+    c64, c16 = workload_oracle(name)
+    assert_close(got, c64, c16, w.K, name)
+    rec = _errstats.record(name, got, c64, c16, w.K)
+    assert abs(rec["mean"] - 1.4e-4) < 0.3e-4, rec
+    assert rec["max"] <= 2.0e-3 + 1e-5, rec
+    assert abs(rec["signed_mean"]) < 2e-5, rec  # round to nearest: no bias toward zero
+    assert abs(rec["var_c64"] - 1.0) < 0.02, rec
     assert abs(float(got.astype(np.float64).var()) - 1.0) < 0.02
 
 
@@ -157,25 +156,15 @@ def test_headline_sampled_parity_and_error_figures():
 
 @pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
 def test_integer_inputs_bit_exact(name):
+    """Integer inputs in {-1, 0, 1} at every workload's full size: every
+    fp32 partial sum is an exact integer, so all outputs must equal the
+    oracle's rne(C64) bit for bit."""
     w = workloads.by_name(name)
     a, b = workloads.small_integers(w.M, w.N, w.K, seed=w.seed)
     print("case int", name, flush=True)
     got = run(a, b)
-    if w.M * w.N * w.K <= 2 ** 38:
-        _, c16 = oracle.gemm_nt(a, b)
-        assert np.array_equal(got.view(np.uint16), c16.view(np.uint16))
-    else:
-        # exact integer product from numpy's float64 matmul over a row slab
-        # (a library routine; integer sums below 2^53 are exact), plus the
-        # oracle on sampled outputs
-        rows = np.arange(0, w.M, 97)
-        ref = a[rows].astype(np.float64) @ b.astype(np.float64).T
-        c16 = oracle.encode_rne(ref).view(np.float16)
-        assert np.array_equal(got[rows].view(np.uint16), c16.view(np.uint16))
-        g = np.random.Generator(np.random.PCG64(5))
-        r, c = g.integers(0, w.M, 4096), g.integers(0, w.N, 4096)
-        e = oracle.encode_rne(oracle.gemm_nt_entries(a, b, r, c))
-        assert np.array_equal(got[r, c].view(np.uint16), e)
+    _, c16 = oracle.gemm_nt(a, b)
+    assert np.array_equal(got.view(np.uint16), c16.view(np.uint16))
 
 
 def test_identity_b_gives_a():
@@ -234,6 +223,105 @@ def test_subnormal_inputs():
     got = run(a, b)
     _, c16 = oracle.gemm_nt(a, b)
     assert np.array_equal(got.view(np.uint16), c16.view(np.uint16))
+
+
+# --------------------------------------------------------- special values --
+#
+# The pages fix only the one fp16 cast of the fp32 accumulator ("0. A Minimal
+# Hopper Matmul", "Walkthrough", "Epilogue").  Read by IEEE 754 rules: a NaN
+# input, Inf * 0 and Inf - Inf give NaN, an Inf term otherwise gives an Inf of
+# its sign, and a finite sum of magnitude >= 65520 rounds to Inf (65520 lies
+# halfway between the largest fp16 value, 65504, and 2^16, and ties go to the
+# even neighbour, 2^16, which overflows).  Products of fp16 values are exact
+# in fp32, and with integer operands every partial sum below 2^24 is exact in
+# any order, so the GPU must match the oracle's rne(C64) bit for bit (NaN by
+# class: its payload and sign are not specified).
+
+SPECIAL_SHAPE = (300, 264, 136)  # partial tiles in M and N, a K tail of 8
+
+
+def assert_same_or_both_nan(got16, c16, label):
+    g, c = got16.view(np.uint16), c16.view(np.uint16)
+    gn, cn = np.isnan(got16.astype(np.float32)), np.isnan(c16.astype(np.float32))
+    assert np.array_equal(gn, cn), "%s: NaN at %d outputs, oracle %d" % (label, gn.sum(), cn.sum())
+    bad = (g != c) & ~gn
+    assert not bad.any(), "%s: %d outputs differ, first at %s" % (label, bad.sum(), np.argwhere(bad)[0])
+
+
+def special_value_inputs():
+    """Integer inputs in {-1, 0, 1} with Inf and NaN planted in A and B: in
+    full K steps, in the K tail, in the last row of B, and pairs that give
+    Inf * 0 and Inf - Inf."""
+    M, N, K = SPECIAL_SHAPE
+    a, b = workloads.small_integers(M, N, K, seed=71)
+    inf, nan = np.float16(np.inf), np.float16(np.nan)
+    a[5, 17] = inf
+    a[9, 100] = -inf
+    a[13, 3] = nan
+    a[40, 130] = inf      # in the K tail (k >= 128)
+    a[299, 0] = -inf      # the last row, in the partial tile row
+    a[30, 10] = inf       # Inf - Inf wherever B[n, 10] = -B[n, 11] != 0
+    a[30, 11] = inf
+    b[7, 17] = 0          # Inf * 0 = NaN at C[5, 7]
+    b[20, 50] = inf       # column 20: +-Inf or NaN by A[m, 50]
+    b[263, 135] = nan     # the last row of B, the last k
+    b[100, 64] = -inf     # the first k of the second K step
+    return a, b
+
+
+def overflow_inputs():
+    """Integer sums that land on and around the fp16 overflow edge and on
+    rounding ties: rows 0 .. 7 of A hold 1 (rows 8 .. 15: -1) at k = 0 .. 3
+    and 0 elsewhere, so C[m, n] = +-(B[n, 0] + .. + B[n, 3]) exactly, with
+    B's first four entries in rows n < 18 fp16 integers that sum to each
+    target; the other rows of A are random in {-1, 0, 1} against those large
+    entries."""
+    M, N, K = SPECIAL_SHAPE
+    a, b = workloads.small_integers(M, N, K, seed=72)
+    targets = [65504, 65505, 65519, 65520, 65521, 65536, 100000, 2049, 2051, 4097, 4098, 4099,
+               32768, 65488, 65496, 65503, 131000, 200000]
+    for n, t in enumerate(targets):
+        parts, r = [], t
+        while r > 0:  # greedy: the largest fp16 integer not above what is left
+            f = np.float16(min(r, 65504))
+            if float(f) > r:
+                f = np.nextafter(f, np.float16(0))
+            parts.append(float(f))
+            r -= float(f)
+        assert len(parts) <= 4 and sum(parts) == t, (t, parts)
+        b[n, :4] = 0
+        b[n, :len(parts)] = np.array(parts, dtype=np.float16)
+    a[:16, :] = 0
+    a[:8, :4] = 1
+    a[8:16, :4] = -1
+    return a, b
+
+
+def test_special_values_every_variant():
+    a, b = special_value_inputs()
+    _, c16 = oracle.gemm_nt(a, b)
+    assert np.isnan(c16.astype(np.float32)).any() and np.isinf(c16.astype(np.float32)).any()
+    print("case special plan", *SPECIAL_SHAPE, flush=True)
+    assert_same_or_both_nan(run(a, b), c16, "plan")
+    for name, vid in variant_ids().items():
+        print("case special", name, flush=True)
+        assert_same_or_both_nan(run(a, b, variant=vid), c16, name)
+
+
+def test_overflow_to_inf_every_variant():
+    a, b = overflow_inputs()
+    _, c16 = oracle.gemm_nt(a, b)
+    c = c16.astype(np.float64)
+    # the edge itself: 65504 stays, 65519 rounds down, 65520 (a tie) overflows
+    assert c[0, 0] == 65504 and c[0, 2] == 65504 and np.isinf(c[0, 3]) and c[8, 0] == -65504
+    assert c[0, 7] == 2048 and c[0, 8] == 2052  # ties to even
+    assert np.isinf(c).sum() > 100 and not np.isnan(c).any()
+    print("case overflow plan", *SPECIAL_SHAPE, flush=True)
+    assert_same_or_both_nan(run(a, b), c16, "plan")
+    for name, vid in variant_ids().items():
+        print("case overflow", name, flush=True)
+        got = run(a, b, variant=vid)
+        assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), name
 
 
 # ------------------------------------------------------------ edge shapes --

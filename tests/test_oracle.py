@@ -333,6 +333,21 @@ def test_workload_inputs_are_reproducible():
     assert a1.dtype == np.float16
 
 
+def test_workload_input_digests_are_pinned():
+    """Every workload's input bytes against the SHA-256 recorded in
+    tests/golden/workload_digests.json (written by make_workload_digests.py
+    beside it), so the oracle, the GPU tests and the benchmark see the same
+    bits on every machine and numpy version."""
+    with open(os.path.join(GOLDEN, "workload_digests.json")) as f:
+        pinned = json.load(f)["digests"]
+    assert set(pinned) == {w.name for w in workloads.WORKLOADS}
+    for w in workloads.WORKLOADS:
+        p = pinned[w.name]
+        assert (p["M"], p["N"], p["K"], p["seed"]) == (w.M, w.N, w.K, w.seed), w.name
+        a, b = workloads.workload_inputs(w)
+        assert workloads.digest(a, b) == p["sha256"], w.name
+
+
 def test_unit_variance_outputs():
     # entries N(0, variance K**-0.5) make Var(C) = K * Var(a) * Var(b) = 1
     w = workloads.WORKLOADS[1]
