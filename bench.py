@@ -3,16 +3,22 @@
 
 One step is one call of ``gemm_nt_f16`` (the whole path: tile scheduling,
 global->LDS staging, MFMA loop, epilogue) on M = N = K = 8192 by default, with
-seeded synthetic fp16 inputs already resident in HBM.  Method, following the
-pages' own ("6. Four Consumers, FP16 Accumulation, and a TMA Epilogue",
-section "Performance"): warm-up launches, a cool-down pause, then a window of
-back-to-back launches bracketed by events on the launch stream.
+seeded synthetic fp16 inputs already resident in HBM.
+
+The engine clock is power-managed: from idle, the first launches run at a
+high clock, the clock then dips below the level it settles at and recovers
+over tens of milliseconds.  So before the --warmup steps the benchmark
+launches back to back for --settle seconds (untimed), and the --steps timed
+launches, bracketed by events on the launch stream, measure the rate the
+chip sustains.  After them it repeats the pages' own protocol ("6. Four
+Consumers, FP16 Accumulation, and a TMA Epilogue", section "Performance": a
+cool-down pause, then 30 back-to-back launches) and reports it beside the
+result as ``pages_protocol``, never as the result.
 
 The line carries a ``roofline`` object for the MFMA kernel (algorithmic
 2*M*N*K flop per launch over the measured launch time, against the dense
 fp16 MFMA peak) and a ``cpu_baseline`` object: the CPU oracle timed on a
-bounded slab of the same product on this host's cores.  After the timed
-window it adds a ``throttle_check`` (the next 100 launches) and a
+bounded slab of the same product on this host's cores.  Last comes a
 ``clock_window``: three seconds of back-to-back launches while amd-smi, run
 from a child process started before this one touches the GPU, samples the
 engine clock and board power, so the result can also be read against the
@@ -241,10 +247,18 @@ def main(argv=None) -> int:
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="square_8192")
     p.add_argument("--variant", type=int, default=-1, help="kernel variant index (-1: automatic)")
-    p.add_argument("--cooldown", type=float, default=3.0, help="seconds idle before the timed window")
+    p.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
+                   help="launch back to back for this long before the warm-up steps (untimed), so the "
+                        "timed window sees the clock the chip sustains")
+    p.add_argument("--cooldown", type=float, default=0.0,
+                   help="seconds idle between the warm-up and the timed window (the pages' protocol "
+                        "pauses 3 s; it is also reported separately, see --pages-protocol)")
+    p.add_argument("--pages-protocol", type=float, default=3.0, metavar="SECONDS",
+                   help="after the timed window, pause this long and time 30 back-to-back launches, as "
+                        "the pages do; reported beside the result (0: skip)")
     p.add_argument("--cpu-rows", type=int, default=8192,
                    help="rows of A in the oracle's timed slab (0 skips the CPU baseline)")
-    p.add_argument("--throttle-check", type=int, default=100, metavar="N",
+    p.add_argument("--throttle-check", type=int, default=0, metavar="N",
                    help="after the timed window, time N more back-to-back launches (0: skip); "
                         "reported beside the result, never as the result")
     p.add_argument("--clock-window", type=float, default=3.0, metavar="SECONDS",
@@ -327,23 +341,37 @@ def measure(args, sampler) -> int:
             binding.gemm_nt_f16(ta, tb, out=out)
 
     stream = torch.cuda.current_stream(dev)
+    settle = None
+    if args.settle > 0:
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.settle:
+            for _ in range(10):
+                step()
+            n += 10
+            torch.cuda.synchronize()
+        settle = {"seconds": time.perf_counter() - t0, "launches": n,
+                  "note": "untimed back-to-back launches before the warm-up steps"}
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     if args.cooldown > 0:
         time.sleep(args.cooldown)
 
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps
+    def window(k):
+        """k back-to-back launches between events on the launch stream:
+        (ms per launch, host wall seconds)."""
+        s0 = torch.cuda.Event(enable_timing=True)
+        e0 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        s0.record(stream)
+        for _ in range(k):
+            step()
+        e0.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(e0) / k, time.perf_counter() - t0
+
+    ms, wall = window(args.steps)
     tflops = w.flops / (ms * 1e-3) / 1e12
     log("bench: %.4f ms per launch (%.1f TFLOP/s, %.1f%% of peak); host wall %.4f ms per step"
         % (ms, tflops, 100 * tflops / PEAK_TFLOPS, 1e3 * wall / args.steps))
@@ -351,23 +379,22 @@ def measure(args, sampler) -> int:
         print("bench.py: non-finite output", file=sys.stderr)
         return 1
 
-    # The engine clock is power-managed: after the idle pause the first
-    # launches run fast, the clock then dips below its settled value and
-    # recovers over ~20 ms.  A longer back-to-back window shows where it
-    # settles; the result above keeps the 30-launch window of the protocol.
+    pages = None
+    if args.pages_protocol > 0:
+        time.sleep(args.pages_protocol)
+        ms_p, _ = window(30)
+        pages = {"cooldown_s": args.pages_protocol, "launches": 30, "ms_per_launch": ms_p,
+                 "tflops": w.flops / (ms_p * 1e-3) / 1e12,
+                 "note": "after an idle pause the clock dips below its settled value for ~20 ms"}
+        log("bench: pages' protocol (%.0f s pause, 30 launches): %.4f ms per launch (%.1f TFLOP/s)"
+            % (args.pages_protocol, ms_p, pages["tflops"]))
+
     throttle = None
     if args.throttle_check > 0:
-        s2 = torch.cuda.Event(enable_timing=True)
-        e2 = torch.cuda.Event(enable_timing=True)
-        s2.record(stream)
-        for _ in range(args.throttle_check):
-            step()
-        e2.record(stream)
-        torch.cuda.synchronize()
-        ms2 = s2.elapsed_time(e2) / args.throttle_check
+        ms2, _ = window(args.throttle_check)
         throttle = {"launches": args.throttle_check, "ms_per_launch": ms2,
                     "tflops": w.flops / (ms2 * 1e-3) / 1e12,
-                    "window": "back-to-back launches right after the timed ones"}
+                    "window": "back-to-back launches after the timed ones"}
         log("bench: next %d launches: %.4f ms per launch (%.1f TFLOP/s)"
             % (args.throttle_check, ms2, throttle["tflops"]))
 
@@ -414,6 +441,10 @@ def measure(args, sampler) -> int:
                    "output": "f16", "kernel": plan, "pct_of_peak": 100 * tflops / PEAK_TFLOPS},
         "roofline": roof,
     }
+    if settle is not None:
+        rec["settle"] = settle
+    if pages is not None:
+        rec["pages_protocol"] = pages
     if throttle is not None:
         rec["throttle_check"] = throttle
     if clock is not None:
