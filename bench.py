@@ -246,7 +246,8 @@ def main(argv=None) -> int:
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="square_8192")
-    p.add_argument("--variant", type=int, default=-1, help="kernel variant index (-1: automatic)")
+    p.add_argument("--variant", default="-1",
+                   help="kernel variant, by index or name (-1: the library's own launch plan)")
     p.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
                    help="launch back to back for this long before the warm-up steps (untimed), so the "
                         "timed window sees the clock the chip sustains")
@@ -326,8 +327,9 @@ def measure(args, sampler) -> int:
     tb = torch.from_numpy(b).to(dev)
     out = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     names = binding.variants()
-    if args.variant >= 0:
-        vid, rows, rest = args.variant, w.M, -1
+    forced = int(args.variant) if args.variant.lstrip("-").isdigit() else names.index(args.variant)
+    if forced >= 0:
+        vid, rows, rest = forced, w.M, -1
     else:  # the library's own plan, as gemm_nt_f16 runs it
         vid, rows, rest = binding.gemm_nt_f16_plan(w.M, w.N, w.K)
     vname = names[vid]
@@ -335,7 +337,7 @@ def measure(args, sampler) -> int:
     log("bench: %s" % plan)
 
     def step():
-        if args.variant >= 0:
+        if forced >= 0:
             binding.gemm_nt_f16_ex(ta, tb, out=out, variant=vid)
         else:
             binding.gemm_nt_f16(ta, tb, out=out)

@@ -72,6 +72,7 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
@@ -126,13 +127,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // renumber ids so each XCD owns one contiguous range of the linear order, then
 // sweep that order in groups of `group_m` tile rows, column by column, so the
 // tiles that run at the same time on one XCD share rows of A and of B.
+// Two other orders exist for comparison: group_m < 0 groups |group_m| tile
+// rows without the XCD renumbering (the pages' grouped raster, made for one
+// L2), and group_m == 0 walks the tiles row by row.
 __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int group_m,
                                             int& tm, int& tn)
 {
+    if (group_m == 0) {
+        tm = pid / tiles_n;
+        tn = pid - tm * tiles_n;
+        return;
+    }
     const int total = tiles_m * tiles_n;
-    const int per = total / kXcds, extra = total % kXcds;
-    const int x = pid % kXcds, local = pid / kXcds;
-    const int lin = x * per + (x < extra ? x : extra) + local;
+    int lin = pid;
+    if (group_m > 0) {
+        const int per = total / kXcds, extra = total % kXcds;
+        const int x = pid % kXcds, local = pid / kXcds;
+        lin = x * per + (x < extra ? x : extra) + local;
+    } else {
+        group_m = -group_m;
+    }
     const int width = group_m * tiles_n;
     const int g = lin / width;
     const int first = g * group_m;
@@ -211,7 +225,8 @@ struct TileShape {
     static_assert(A_LOADS * LOADERS * 1024 == A_BYTES, "A tile must split evenly over loading waves");
     static_assert(B_LOADS * LOADERS * 1024 == B_BYTES, "B tile must split evenly over loading waves");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
-    static_assert(STAGES >= 2 && LOADS * (STAGES - 2) <= 63, "vmcnt holds at most 63");
+    static_assert(STAGES >= 1 && LOADS * (STAGES - 2) <= 63, "vmcnt holds at most 63");
+    static_assert(STAGES >= 2 || (EARLY_ == 0 && DIST_ == 1), "a single stage is loaded, then computed");
     static_assert(EARLY >= 0 && EARLY <= LOADS && (EARLY == 0 || STAGES >= 3),
                   "early loads need a free stage one step ahead");
     static_assert(DIST >= 1 && DIST <= KK, "fragments are read 1 .. KK sub-steps ahead");
@@ -552,79 +567,97 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     // steps, so the fragment set parity is known at compile time.
     auto main_loop = [&](auto tag) {
         constexpr bool LD = decltype(tag)::value;
-        if constexpr (T::EARLY == 0) {
-            // every stage is free at the start: fill them all, then wait
-            // for step 0 only
+        if constexpr (T::STAGES == 1) {
+            // One stage, nothing overlaps: load a step, wait until every
+            // wave's loads have landed, compute it, and wait until every wave
+            // is done reading before the next step's loads overwrite it (the
+            // first kernel of "0. A Minimal Hopper Matmul": the copy runs,
+            // then everyone waits).  A ladder rung only.
+            for (int ks = 0; ks < nk; ++ks) {
+                if constexpr (LD) issue_loads(0, ks);
+                lds_barrier<0>();
 #pragma unroll
-            for (int s = 0; s < T::STAGES; ++s)
-                if constexpr (LD) issue_loads(s, s);
-            lds_barrier<T::LOADS * (T::STAGES - 1)>();
+                for (int kk = 0; kk < T::KK; ++kk) {
+                    read_frags(0, smem, kk);
+                    mma(0, kk);
+                }
+                lds_barrier<0>();
+            }
         } else {
-            // the early part of step STAGES - 1 goes out during step 0
+            if constexpr (T::EARLY == 0) {
+                // every stage is free at the start: fill them all, then wait
+                // for step 0 only
 #pragma unroll
-            for (int s = 0; s < T::STAGES - 1; ++s)
-                if constexpr (LD) issue_loads(s, s);
-            lds_barrier<T::LOADS * (T::STAGES - 2)>();
-            if constexpr (LD) issue_load_range(T::STAGES - 1, T::STAGES - 1, 0, T::LATE);
-        }
+                for (int s = 0; s < T::STAGES; ++s)
+                    if constexpr (LD) issue_loads(s, s);
+                lds_barrier<T::LOADS * (T::STAGES - 1)>();
+            } else {
+                // the early part of step STAGES - 1 goes out during step 0
 #pragma unroll
-        for (int kk = 0; kk < T::DIST; ++kk) read_frags(0, smem, kk);
+                for (int s = 0; s < T::STAGES - 1; ++s)
+                    if constexpr (LD) issue_loads(s, s);
+                lds_barrier<T::LOADS * (T::STAGES - 2)>();
+                if constexpr (LD) issue_load_range(T::STAGES - 1, T::STAGES - 1, 0, T::LATE);
+            }
+#pragma unroll
+            for (int kk = 0; kk < T::DIST; ++kk) read_frags(0, smem, kk);
 
-        int cur = 0;  // stage of step ks
-        auto step = [&](int ks, auto parity) {
-            constexpr int P = decltype(parity)::value;
-            constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
-            const unsigned char* base = smem + cur * T::STAGE_BYTES;
-            const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
-            const int prv = cur == 0 ? T::STAGES - 1 : cur - 1;  // free since the last barrier
-            // Each sub-step is its own scheduling region (fenced with
-            // sched_barrier), so MFMAs of different sub-steps never
-            // interleave into back-to-back dependent pairs.
+            int cur = 0;  // stage of step ks
+            auto step = [&](int ks, auto parity) {
+                constexpr int P = decltype(parity)::value;
+                constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
+                const unsigned char* base = smem + cur * T::STAGE_BYTES;
+                const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
+                const int prv = cur == 0 ? T::STAGES - 1 : cur - 1;  // free since the last barrier
+                // Each sub-step is its own scheduling region (fenced with
+                // sched_barrier), so MFMAs of different sub-steps never
+                // interleave into back-to-back dependent pairs.
 #pragma unroll
-            for (int kk = 0; kk < T::KK - T::DIST; ++kk) {
-                constexpr int E = LD ? T::EARLY : 0;
-                constexpr int R1 = T::KK - T::DIST > 0 ? T::KK - T::DIST : 1;
-                const int e0 = E * kk / R1, e1 = E * (kk + 1) / R1;  // this sub-step's early loads
-                read_frags(P, base, kk + T::DIST);
-                mma(P, kk);
-                if constexpr (E > 0) issue_load_range(prv, ks + T::STAGES - 1, T::LATE + e0, e1 - e0);
-                __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
+                for (int kk = 0; kk < T::KK - T::DIST; ++kk) {
+                    constexpr int E = LD ? T::EARLY : 0;
+                    constexpr int R1 = T::KK - T::DIST > 0 ? T::KK - T::DIST : 1;
+                    const int e0 = E * kk / R1, e1 = E * (kk + 1) / R1;  // this sub-step's early loads
+                    read_frags(P, base, kk + T::DIST);
+                    mma(P, kk);
+                    if constexpr (E > 0) issue_load_range(prv, ks + T::STAGES - 1, T::LATE + e0, e1 - e0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
 #pragma unroll
-                for (int i = 0; i < G; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-                    sched_vmem<0>((e1 - e0) * (i + 1) / G - (e1 - e0) * i / G);  // loads
+                    for (int i = 0; i < G; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+                        sched_vmem<0>((e1 - e0) * (i + 1) / G - (e1 - e0) * i / G);  // loads
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+                lds_barrier<T::LOADS * (T::STAGES - 2)>();
                 __builtin_amdgcn_sched_barrier(0);
-            }
-            lds_barrier<T::LOADS * (T::STAGES - 2)>();
-            __builtin_amdgcn_sched_barrier(0);
-            const unsigned char* next = smem + nxt * T::STAGE_BYTES;
+                const unsigned char* next = smem + nxt * T::STAGE_BYTES;
 #pragma unroll
-            for (int d = 0; d < T::DIST; ++d) {
-                constexpr int L = LD ? T::LATE : 0;
-                const int l0 = L * d / T::DIST, l1 = L * (d + 1) / T::DIST;  // this sub-step's loads
-                read_frags(1 - P, next, d);
-                mma(P, T::KK - T::DIST + d);
-                if constexpr (L > 0) issue_load_range(cur, ks + T::STAGES, l0, l1 - l0);
-                __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
+                for (int d = 0; d < T::DIST; ++d) {
+                    constexpr int L = LD ? T::LATE : 0;
+                    const int l0 = L * d / T::DIST, l1 = L * (d + 1) / T::DIST;  // this sub-step's loads
+                    read_frags(1 - P, next, d);
+                    mma(P, T::KK - T::DIST + d);
+                    if constexpr (L > 0) issue_load_range(cur, ks + T::STAGES, l0, l1 - l0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
 #pragma unroll
-                for (int i = 0; i < G; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);          // one MFMA
-                    sched_vmem<1>((l1 - l0) * (i + 1) / G - (l1 - l0) * i / G);  // loads
+                    for (int i = 0; i < G; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);          // one MFMA
+                        sched_vmem<1>((l1 - l0) * (i + 1) / G - (l1 - l0) * i / G);  // loads
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                cur = nxt;
+            };
+            if constexpr (ALT) {
+                for (int ks = 0; ks < nk; ++ks) step(ks, Int<0>{});
+            } else {
+                int ks = 0;
+                for (; ks + 1 < nk; ks += 2) {
+                    step(ks, Int<0>{});
+                    step(ks + 1, Int<1>{});
+                }
+                if (ks < nk) step(ks, Int<0>{});
             }
-            cur = nxt;
-        };
-        if constexpr (ALT) {
-            for (int ks = 0; ks < nk; ++ks) step(ks, Int<0>{});
-        } else {
-            int ks = 0;
-            for (; ks + 1 < nk; ks += 2) {
-                step(ks, Int<0>{});
-                step(ks + 1, Int<1>{});
-            }
-            if (ks < nk) step(ks, Int<0>{});
         }
     };
     if (nk > 0) {
@@ -886,16 +919,23 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
 // barrier waits on its vmcnt, which would also wait for any store it had
 // issued; the non-loading waves never wait on theirs, so the stores drain
 // while the next tile computes.  Host side: K > 64 (two steps at least),
-// C rows allow aligned 16-byte stores.
-template <class T, int RS, int LS>
+// C rows allow aligned 16-byte stores.  With DIRECT (a ladder rung only) the
+// LDS staging is skipped: every wave stores its own accumulators as 8-byte
+// pieces, four consecutive columns of one row per lane, the way "6. Four
+// Consumers, FP16 Accumulation, and a TMA Epilogue" ("Serialized
+// Shared-Memory Epilogue") describes stores straight from registers.
+template <class T, int RS, int LS, bool DIRECT = false>
 __global__ void __launch_bounds__(T::THREADS, 1)
 gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                             _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
                             int group_m, int c_vec)
 {
-    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && T::WAVES == 8 && T::LOADERS == 4 &&
-                      T::WAVES_M == 2 && T::NG == 1,
-                  "16x16x32 MFMAs, two sub-steps per step, 2 x 4 waves of which 4 load");
+    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && T::LOADERS == 4 &&
+                      (T::WAVES == 8 || T::WAVES == 4) && T::WAVES_M == 2 && T::NG == 1,
+                  "16x16x32 MFMAs, two sub-steps per step, 2 x 4 waves of which 4 load, or 2 x 2 "
+                  "waves that all load");
+    // with eight waves the four that never load store C; with four, all do
+    constexpr bool ALL_STORE = T::WAVES == T::LOADERS;
     constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
     constexpr int R = T::FM + T::FN;  // fragment reads per sub-step
     constexpr int SLOT = T::A_BYTES;  // one operand tile of one step
@@ -969,23 +1009,23 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
 
     half8_t fa[2][T::FM], fb[2][T::FN];
     typename T::acc_t acc[T::FM][T::FN];
-    // Zero the accumulators in place: an MFMA of zero operands with an inline
-    // zero as its C input.  (Plain writes could be moved next to the first
-    // accumulating MFMA, whose asm hides the VALU-to-MFMA hazard from the
-    // compiler; pinning them in AGPRs with asm operands makes the register
-    // allocator spill.)  The zero operand is written by a VALU move, which an
-    // MFMA may read only a few wait states later: the compiler cannot see
-    // that hazard through the asm, so each statement waits first.
-    auto zero_acc = [&]() __attribute__((always_inline)) {
-        const half8_t z = {};
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-                asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_f16 %0, %1, %1, 0"
-                             : "=a"(acc[i][j])
-                             : "v"(z)
-                             : "memory");
+    // Accumulators are cleared in place by an MFMA of zero fragments with an
+    // inline zero as its C input: once at the start, and then block by block
+    // in each epilogue, right after the block has been read out, so the
+    // clearing MFMAs run on the matrix core while the wave converts and
+    // stores the rest of the tile.  (Plain writes could be moved next to the
+    // first accumulating MFMA, whose asm hides the VALU-to-MFMA hazard from
+    // the compiler; pinning them in AGPRs with asm operands makes the
+    // register allocator spill.)  The zero fragment is written by VALU moves,
+    // which an MFMA may read only a few wait states later; the asm statement
+    // it passes through waits that long, once.
+    auto zero_frag = [&]() __attribute__((always_inline)) {
+        half8_t z = {};
+        asm volatile("s_nop 4" : "+v"(z));
+        return z;
+    };
+    auto clear = [&](int i, int j, const half8_t& z) __attribute__((always_inline)) {
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %1, 0" : "=a"(acc[i][j]) : "v"(z) : "memory");
     };
 
     // fragment read `idx` of set `set`, in the order the MFMAs below first
@@ -1028,6 +1068,38 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
     // buffer stores (as in epilogue_lds: one 32-bit offset per store; rows
     // past M fall outside the buffer and columns past N get an offset outside
     // it, so neither is written).
+    // Epilogue without staging: every wave converts its accumulators and
+    // stores them itself, lane l writing columns 4 * (l / 16) .. + 3 of row
+    // l % 16 of each 16 x 16 block as one 8-byte nontemporal buffer store
+    // (rows past M outside the buffer, columns past N sent outside it).
+    auto epilogue_direct = [&](int cm0, int cn0) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int e_row = ln % T::MI, e_hi = ln / T::MI;
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(C + (size_t)cm0 * N, (uint32_t)min(T::BM, M - cm0) * (uint32_t)N * 2u);
+        uint32_t pitch_c = (uint32_t)N * 2u;
+        asm volatile("" : "+s"(pitch_c)::"memory");
+        const half8_t z = zero_frag();
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+            const int n = cn0 + wn * T::WTN + j * T::MI + 4 * e_hi;
+            const uint32_t vcol = n < N ? (uint32_t)n * 2u : kOob;
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i) {
+                const uint32_t r = (uint32_t)(wm * T::WTM + i * T::MI + e_row);
+                half4_t v;
+                v[0] = (_Float16)acc[i][j][0];
+                v[1] = (_Float16)acc[i][j][1];
+                v[2] = (_Float16)acc[i][j][2];
+                v[3] = (_Float16)acc[i][j][3];
+                clear(i, j, z);
+                const uint32_t off = vcol == kOob ? kOob : vcol + r * pitch_c;
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rc, off, 0, kPolicyNt);
+            }
+        }
+    };
+
     auto epilogue = [&](unsigned char* s0, unsigned char* s1, int cm0, int cn0, bool storer)
                         __attribute__((always_inline)) {
         constexpr int PITCH = T::BN * 2;           // bytes per staged row
@@ -1036,13 +1108,13 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
         constexpr int HALF = T::FM / 2;            // MFMA block rows per round
         constexpr int SROWS = SLOT / PITCH;        // staged rows per slot
         constexpr int RPL = 1024 / PITCH;          // rows per wave-wide 1 KiB read
-        constexpr int STORERS = T::WAVES - T::LOADERS;
+        constexpr int STORERS = ALL_STORE ? T::WAVES : T::WAVES - T::LOADERS;
         constexpr int ITERS = 2 * SROWS / RPL / STORERS;  // reads per storing wave per round
         static_assert(HALF * T::MI == SROWS && ITERS * RPL * STORERS == 2 * SROWS && ITERS % 4 == 0 &&
                           ITERS * RPL * 2 == SROWS,
                       "a round fills both slots, each storing wave reads half a slot");
         unsigned char* mine = wm == 0 ? s0 : s1;
-        const int sw = wave - T::LOADERS;
+        const int sw = ALL_STORE ? wave : wave - T::LOADERS;
         // the lane index laundered: offsets derived from it are computed
         // here rather than kept (or spilled) through the K loop
         int ln = lane;
@@ -1057,6 +1129,7 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
         const int n = cn0 + lc * 8;
         const uint32_t vbase = n < N ? ((uint32_t)lr * (uint32_t)N + (uint32_t)n) * 2u : kOob;
         const unsigned char* rd = (sw < STORERS / 2 ? s0 : s1) + (sw % 2) * (SROWS / 2) * PITCH;
+        const half8_t z = zero_frag();
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -1071,6 +1144,7 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
                     v[1] = (_Float16)acc[h * HALF + i][j][1];
                     v[2] = (_Float16)acc[h * HALF + i][j][2];
                     v[3] = (_Float16)acc[h * HALF + i][j][3];
+                    clear(h * HALF + i, j, z);
                     *(half4_t*)(lrow + (((col >> 3) ^ (x & SW)) << 4) + (col & 4) * 2) = v;
                 }
             }
@@ -1102,7 +1176,13 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
         constexpr bool LD = decltype(ldtag)::value;
         // a step's barrier: this wave's loads but the last A tile have landed
         constexpr int VMW = LD ? T::A_LOADS : 63;
-        zero_acc();
+        {
+            const half8_t z = zero_frag();
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j) clear(i, j, z);
+        }
         // steps 0 and 1 of the first tile into slots 0 .. 3, then wait for step 0
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -1160,14 +1240,16 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
             // (and keep the scheduler from moving their reads above the wait)
             __builtin_amdgcn_sched_barrier(0);
-            epilogue(slot(0), slot(1), cm0, cn0, !LD);
+            if constexpr (DIRECT)
+                epilogue_direct(cm0, cn0);
+            else
+                epilogue(slot(0), slot(1), cm0, cn0, ALL_STORE || !LD);
             if (next >= total) break;
             // B of the next tile's step 1 where the last step's A was
 #pragma unroll
             for (int l = T::A_LOADS; l < T::LOADS; ++l)
                 if constexpr (LD) issue_load(sa, lbase + 1, l, Flag<true>{}, row_bytes);
             advance();
-            zero_acc();
 #pragma unroll
             for (int idx = 0; idx < R; ++idx) read_one(0, slot(0), slot(1), idx);
             tile = next;
@@ -1259,6 +1341,22 @@ int launch_mfma(const void* A, const void* B, void* C, int64_t M, int64_t N, int
     return (int)hipGetLastError();
 }
 
+// The same with dynamic LDS padding the workgroup to a whole CU's 160 KiB,
+// so only one workgroup runs per CU (a ladder rung: the single-stage kernel
+// without other workgroups to overlap its copies).
+template <class T>
+int launch_mfma_one_per_cu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int group_m,
+                           hipStream_t stream)
+{
+    const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
+    if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
+    const int c_vec = c_store_mode(N, C);
+    hipLaunchKernelGGL((gemm_nt_f16_mfma<T>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS),
+                       160 * 1024 - T::LDS_BYTES, stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C,
+                       (int)M, (int)N, (int)K, (int)tiles_m, (int)tiles_n, group_m, c_vec);
+    return (int)hipGetLastError();
+}
+
 template <class T, int RS, int LS, bool SLOTS5 = false>
 int launch_ordered(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int group_m,
                    hipStream_t stream)
@@ -1276,7 +1374,7 @@ int launch_ordered(const void* A, const void* B, void* C, int64_t M, int64_t N, 
 // where its conditions hold, else the one-tile-per-workgroup 5-slot kernel.
 // Its epilogue is faster than the other's even with one tile per workgroup
 // (4096^3: +1%).
-template <class T, int RS, int LS>
+template <class T, int RS, int LS, bool DIRECT = false>
 int launch_ordered_persist(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int group_m,
                            hipStream_t stream)
 {
@@ -1289,7 +1387,7 @@ int launch_ordered_persist(const void* A, const void* B, void* C, int64_t M, int
     // (C offsets are 32-bit and columns past N are sent to kOob: N <= 2^22)
     if ((c_vec & 3) != 2 || K <= T::BK || N > (int64_t(1) << 22))
         return launch_ordered<T, RS, LS, true>(A, B, C, M, N, K, group_m, stream);
-    hipLaunchKernelGGL((gemm_nt_f16_ordered_persist<T, RS, LS>), dim3((unsigned)grid), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_nt_f16_ordered_persist<T, RS, LS, DIRECT>), dim3((unsigned)grid), dim3(T::THREADS), 0,
                        stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N, (int)K,
                        (int)tiles_m, (int)tiles_n, group_m, c_vec);
     return (int)hipGetLastError();
@@ -1341,11 +1439,23 @@ constexpr Variant kVariants[] = {
     {"mfma16_256x256x64_w8_s2_l4_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w8_l4_mi16, 2, 2>},
     {"mfma16_256x256x64_w8_r5_l4_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w8_l4_mi16, 2, 2, true>},
     {"mfma16_256x256x64_w8_r5_l4_persistent", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2>},
+    {"mfma16_256x256x64_w8_r5_l4_persistent_group4", 256, 256, 4, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2>},
+    {"mfma16_256x256x64_w8_r5_l4_persistent_noxcd", 256, 256, -8, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2>},
+    {"mfma16_256x256x64_w8_r5_l4_persistent_linear", 256, 256, 0, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2>},
+    {"mfma16_256x256x64_w8_r5_l4_persistent_direct", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2, true>},
+    {"mfma16_256x256x64_w4_r5_persistent", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 4, 8>},
+    {"mfma16_256x256x64_w4_r5_persistent_rs2", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8>},
+    {"mfma16_256x256x64_w4_r5_persistent_rs3", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 3, 8>},
+    {"mfma16_256x256x64_w4_r5_persistent_rs1", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 1, 8>},
+    {"mfma16_256x256x64_w4_r5_persistent_rs2_ls6", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 6>},
     {"mfma16_256x128x64_w8_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_256x128x64_w8x_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 4, 2, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_128x128x64_w8_s3_l4_ordered", 128, 128, 8, launch_ordered<TileShape<128, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4_mi16>},
     {"mfma16_256x128x64_w8_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w8_mi16>},
+    {"mfma16_128x128x64_w4_s1", 128, 128, 8, launch_mfma<TileShape<128, 128, 64, 2, 2, 1, 2, 0, 0, 1, 16>>},
+    {"mfma16_128x128x64_w4_s1_one_per_cu", 128, 128, 8,
+     launch_mfma_one_per_cu<TileShape<128, 128, 64, 2, 2, 1, 2, 0, 0, 1, 16>>},
     {"mfma16_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4_mi16>},
     {"mfma16_128x128x64_w8_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w8_mi16>},
     {"mfma16_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4_mi16>},

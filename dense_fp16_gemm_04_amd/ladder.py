@@ -1,27 +1,50 @@
-"""Ablation ladder: every kernel variant of the library on one workload.
+"""Ablation ladder: the design steps of the pages, re-made for CDNA4, timed
+and counted on one workload.
 
-Each variant is one design choice away from its neighbours (tile size, wave
-count, ring depth, fragment read distance, which waves load, persistence,
-hand-scheduled issue order), so the table shows what each choice is worth on
-MI355X.  The ladder follows the sequence of design steps the pages walk
-through ("0. A Minimal Hopper Matmul" to "6. Four Consumers, FP16
-Accumulation, and a TMA Epilogue", section "Summary"), re-made for CDNA4.
+The pages build their kernel in steps ("0. A Minimal Hopper Matmul" through
+"6. Four Consumers, FP16 Accumulation, and a TMA Epilogue", section
+"Summary"): a first tiled kernel whose copy and math never overlap, then a
+multi-stage ring, producer/consumer warps, a larger tile, more consumers,
+a grouped tile raster and a staged epilogue.  The rungs below take the same
+steps with this library's kernels, each one design choice away from the
+rung before it; the side rows change one thing of the default kernel.
 
 Run (needs a GPU):
 
     python -m dense_fp16_gemm_04_amd.ladder [--workload square_8192]
 
-Under rocprofv3, with one counter set per run, and then summarised (no GPU
-needed for the summary):
+Each kernel is launched back to back for --settle seconds, then --warmup
+and --launches timed launches (events on the launch stream), so every row
+is read at the clock the chip sustains under that kernel.  Counters come
+from separate runs under rocprofv3, one counter set per run, with no settle
+(every launch is then a counted dispatch), summarised without a GPU:
 
-    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_LDS_BANK_CONFLICT \\
-        SQ_LDS_IDX_ACTIVE --output-format csv -d DIR1 -o run -- \\
-        python3 -m dense_fp16_gemm_04_amd.ladder --launches 2 --warmup 1 --cooldown 0
-    python -m dense_fp16_gemm_04_amd.ladder --summarize DIR1 [DIR2 ...]
+    rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY \\
+        SQ_INSTS_LDS SQ_INSTS_SALU SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE \\
+        --output-format csv -d DIR1 -o run -- \\
+        python3 -m dense_fp16_gemm_04_amd.ladder --settle 0 --warmup 1 --launches 2
+    rocprofv3 --pmc GRBM_GUI_ACTIVE TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_WRREQ_sum \\
+        TCC_EA0_WRREQ_64B_sum --output-format csv -d DIR2 -o run -- \\
+        python3 -m dense_fp16_gemm_04_amd.ladder --settle 0 --warmup 1 --launches 2
+    rocprofv3 --pmc GRBM_GUI_ACTIVE TCC_HIT_sum TCC_REQ_sum --output-format csv -d DIR3 \\
+        -o run -- python3 -m dense_fp16_gemm_04_amd.ladder --settle 0 --warmup 1 --launches 2
+    python -m dense_fp16_gemm_04_amd.ladder --summarize DIR1 DIR2 DIR3 --warmup 1 --launches 2 \\
+        [--times ladder.json]
 
-The summary assigns GEMM dispatches to variants in launch order, which this
-script fixes: every variant gets warmup + launches dispatches, in table
-order, and nothing else launches a kernel whose name contains gemm_nt_f16.
+The summary assigns GEMM dispatches to rows in launch order, which this
+script fixes: every row gets warmup + launches dispatches, in table order,
+and nothing else launches a kernel whose name contains gemm_nt_f16.
+
+Counter readings (GRBM_GUI_ACTIVE counts cycles on each of the 8 XCDs; the
+matrix-core busy cycles, per SIMD, are over 1024 SIMDs): clock =
+GRBM_GUI_ACTIVE / 8 / kernel time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+(GRBM_GUI_ACTIVE / 8 * 1024); bytes read beyond L2 =
+32 * TCC_EA0_RDREQ_DRAM_32B_sum and bytes written = 64 * TCC_EA0_WRREQ_64B_sum
++ 32 * (TCC_EA0_WRREQ_sum - TCC_EA0_WRREQ_64B_sum), factors read off a plain
+1 GiB device copy, which these counters report as exactly 1 GiB read and
+1 GiB written.  The memory-side cache (MALL) sits behind that point, so
+these are requests that leave the L2s for the memory controller: an upper
+bound on HBM traffic.
 """
 from __future__ import annotations
 
@@ -30,6 +53,7 @@ import csv
 import glob
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -37,38 +61,52 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# What each variant changes.  mfma32 variants use v_mfma_f32_32x32x16_f16,
-# mfma16 ones v_mfma_f32_16x16x32_f16.
-RUNGS = {
-    "simple_f32_per_element": "one thread per output, no tiling (the naive baseline)",
-    "mfma32_64x64x64_w4_s3": "64x64 tile, 4 waves, 3-stage ring",
-    "mfma32_128x128x64_w4_s3": "128x128 tile: 2x the reuse per loaded byte",
-    "mfma32_256x128x64_w4_s3": "256x128 tile",
-    "mfma32_256x256x64_w4_s2": "256x256 tile, 4 waves (1 per SIMD, 256 accumulators each), 2 stages",
-    "mfma32_256x256x64_w8_s2": "256x256 tile, 8 waves (2 per SIMD, 128 accumulators each)",
-    "mfma32_256x256x32_w8_s5": "same, BK 32 with a 5-stage ring (loads 4 steps ahead)",
-    "mfma32_256x256x32_w8_s4_d2": "BK 32, 4 stages, fragments read a whole step ahead, loads spread over the step",
-    "mfma32_256x256x64_w8_s2_l4": "only 4 of the 8 waves issue global->LDS loads (a producer/consumer split)",
-    "mfma32_256x256x32_w4_s5_e4": "4 waves, BK 32, 5 stages, half of each step's loads issued a step early",
-    "mfma16_256x256x64_w4_s2": "16x16x32 MFMAs, 4 waves (1 per SIMD, 128x128 each, accumulators in all 256 AGPRs)",
-    "mfma16_256x256x64_w8_s2": "16x16x32 MFMAs, 8 waves (2 per SIMD, 128x64 each)",
-    "mfma16_256x256x32_w8_s4": "16x16x32 MFMAs, 8 waves, BK 32 with a 4-stage ring",
-    "mfma16_256x256x64_w8x_s2": "16x16x32 MFMAs, 8 waves laid out 4x2 (64x128 each)",
-    "mfma16_256x256x64_w8_s2_l4": "16x16x32 MFMAs, 8 waves, 4 of them loading",
-    "mfma16_256x256x64_w4_s2_ordered": "4 waves again, every read and load placed by hand, one per 4 MFMAs",
-    "mfma16_256x256x64_w8_s2_l4_ordered": "8 waves, 4 loading, every read and load placed by hand",
-    "mfma16_256x256x64_w8_r5_l4_ordered": "same with a 5-slot ring: A loads half a step earlier, loads over the whole step",
-    "mfma16_256x256x64_w8_r5_l4_persistent": "same, persistent: the next tile's first steps load during this tile's last, half the waves store C: the default",
-    "mfma16_256x128x64_w4_s3": "16x16x32 MFMAs, 256x128 tile, 4 waves",
-    "mfma16_256x128x64_w8_s3": "16x16x32 MFMAs, 256x128 tile, 8 waves",
-    "mfma16_256x128x64_w4_s3_ordered": "256x128 tile, 4 waves, issue order fixed by hand",
-    "mfma16_256x128x64_w8_s3_l4_ordered": "256x128 tile, 8 waves (2x4, 128x32 each), 4 loading, issue order fixed by hand",
-    "mfma16_256x128x64_w8x_s3_l4_ordered": "same with the waves laid out 4x2 (64x64 each: a fifth fewer LDS reads per MFMA; default for one GPU's share)",
-    "mfma16_128x128x64_w4_s3": "16x16x32 MFMAs, 128x128 tile, 4 waves",
-    "mfma16_128x128x64_w8_s3": "16x16x32 MFMAs, 128x128 tile, 8 waves",
-    "mfma16_128x128x64_w8_s3_l4_ordered": "128x128 tile, 8 waves, 4 loading, issue order fixed by hand (default for mid sizes)",
-    "mfma16_64x64x64_w4_s3": "16x16x32 MFMAs, 64x64 tile (default for small sizes)",
-}
+# (variant, rung, what it adds to the rung above; the pages' step it mirrors)
+LADDER = [
+    ("simple_f32_per_element", "R0",
+     "one thread per output, fp32 FMAs from global memory: no tiling, no matrix cores"),
+    ("mfma16_128x128x64_w4_s1", "R1",
+     "128x128 tiles in LDS, 4 waves of 16x16x32 MFMAs; one stage: load, wait, compute "
+     "(V0: the copy runs, then everyone waits)"),
+    ("mfma16_128x128x64_w4_s3", "R2",
+     "3-stage ring: the loads of later steps overlap the MFMAs (V2's multi-stage ring)"),
+    ("mfma16_128x128x64_w8_s3_l4_ordered", "R3",
+     "8 waves, 4 of them issue the loads, every instruction placed by hand "
+     "(V3's warp specialization: on CDNA4 the loading waves also compute)"),
+    ("mfma16_256x128x64_w8x_s3_l4_ordered", "R4",
+     "256x128 tile: more reuse per loaded byte (V5's 128x256 with two consumer groups)"),
+    ("mfma16_256x256x64_w8_s2_l4_ordered", "R5",
+     "256x256 tile, 2-stage ring (V6's tile; the accumulators fill half the register file)"),
+    ("mfma16_256x256x64_w8_r5_l4_ordered", "R6",
+     "five single-operand LDS slots: a step's loads spread over the whole step"),
+    ("mfma16_256x256x64_w8_r5_l4_persistent", "R7",
+     "persistent: one workgroup per CU walks its tiles, the next tile's loads start "
+     "under this tile's last steps, C staged through LDS (the default)"),
+]
+
+# (variant, what differs from the default kernel, R7)
+SIDE = [
+    ("mfma16_256x256x64_w8_r5_l4_persistent_direct",
+     "C stored straight from registers as 8-byte pieces, no LDS staging "
+     "(V6's 'Serialized Shared-Memory Epilogue', undone)"),
+    ("mfma16_256x256x64_w8_r5_l4_persistent_group4",
+     "raster groups of 4 tile rows instead of 8 (V5's width; V6 raised it to 8)"),
+    ("mfma16_256x256x64_w8_r5_l4_persistent_noxcd",
+     "the pages' grouped raster (8 rows) without renumbering tiles per XCD"),
+    ("mfma16_256x256x64_w8_r5_l4_persistent_linear",
+     "tiles in row-major order: no grouped raster, no XCD renumbering"),
+    ("mfma16_256x256x64_w4_r5_persistent",
+     "4 waves of 128x128 (one per SIMD, accumulators in all 256 AGPRs): "
+     "a third fewer LDS reads per MFMA"),
+    ("mfma16_256x256x64_w8_s2",
+     "compiler-scheduled 256x256, 8 waves, all loading, 2-stage ring (16x16x32 MFMAs)"),
+    ("mfma32_256x256x64_w8_s2",
+     "the same with 32x32x16 MFMAs"),
+]
+
+
+def rows():
+    return [(v, r, w) for v, r, w in LADDER] + [(v, "side", w) for v, w in SIDE]
 
 
 def run(args) -> int:
@@ -87,85 +125,116 @@ def run(args) -> int:
     tb = torch.from_numpy(b).to(dev)
     out = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     names = binding.variants()
-    order = [n for n in names if n != "simple_f32_per_element" or args.with_simple]
-    rows = []
     stream = torch.cuda.current_stream(dev)
-    for name in order:
+    table = []
+    for name, rung, what in rows():
         vid = names.index(name)
-        for _ in range(args.warmup):
+
+        def step():
             binding.gemm_nt_f16_ex(ta, tb, out=out, variant=vid)
+
+        warmup, launches = args.warmup, args.launches
+        t0 = time.perf_counter()
+        first = True
+        while args.settle > 0 and time.perf_counter() - t0 < args.settle:
+            step()
+            torch.cuda.synchronize()
+            if first and time.perf_counter() - t0 > 0.02:  # a slow rung (the per-element kernel)
+                warmup, launches = 1, 3
+            first = False
+        for _ in range(warmup):
+            step()
         torch.cuda.synchronize()
-        if args.cooldown > 0:
-            time.sleep(args.cooldown)
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record(stream)
-        for _ in range(args.launches):
-            binding.gemm_nt_f16_ex(ta, tb, out=out, variant=vid)
+        for _ in range(launches):
+            step()
         e.record(stream)
         torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / args.launches
-        rows.append({"variant": name, "ms": ms, "tflops": w.flops / ms / 1e9,
-                     "rung": RUNGS.get(name, "")})
-        print("ladder: %-32s %8.4f ms %8.1f TFLOP/s" % (name, ms, w.flops / ms / 1e9),
+        ms = s.elapsed_time(e) / launches
+        table.append({"variant": name, "rung": rung, "ms": ms, "tflops": w.flops / ms / 1e9, "launches": launches,
+                      "what": what})
+        print("ladder: %-4s %-46s %9.4f ms %8.1f TFLOP/s" % (rung, name, ms, w.flops / ms / 1e9),
               file=sys.stderr, flush=True)
-    print(json.dumps({"workload": w.name, "warmup": args.warmup, "launches": args.launches,
-                      "rows": rows}), flush=True)
+    print(json.dumps({"workload": w.name, "settle": args.settle, "warmup": args.warmup,
+                      "launches": args.launches, "rows": table}), flush=True)
     return 0
 
 
-def summarize(dirs, warmup, launches, with_simple) -> int:
-    from dense_fp16_gemm_04_amd import binding
+def _dispatches(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("ladder: no counter_collection.csv under %s" % d)
+    disp = {}
+    for r in csv.DictReader(open(files[0])):
+        if "gemm_nt_f16" not in r["Kernel_Name"]:
+            continue
+        e = disp.setdefault(int(r["Dispatch_Id"]),
+                            {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        e[r["Counter_Name"]] = float(r["Counter_Value"])
+    return [disp[k] for k in sorted(disp)]
 
-    names = [n for n in binding.variants() if n != "simple_f32_per_element" or with_simple]
+
+def summarize(dirs, warmup, launches, times=None, workload="square_8192") -> int:
+    from dense_fp16_gemm_04_amd import workloads
+
+    w = workloads.by_name(workload)
+    order = rows()
     per = warmup + launches
-    table = {n: {} for n in names}
+    table = {v: {} for v, _, _ in order}
     for d in dirs:
-        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-        if not files:
-            print("ladder: no counter_collection.csv under %s" % d, file=sys.stderr)
-            return 1
-        rows = list(csv.DictReader(open(files[0])))
-        disp = {}
-        for r in rows:
-            if "gemm_nt_f16" not in r["Kernel_Name"]:
-                continue
-            disp.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
-        ids = sorted(disp)
-        if len(ids) != per * len(names):
-            print("ladder: %s holds %d GEMM dispatches, expected %d" % (d, len(ids), per * len(names)),
+        disp = _dispatches(d)
+        if len(disp) != per * len(order):
+            print("ladder: %s holds %d GEMM dispatches, expected %d" % (d, len(disp), per * len(order)),
                   file=sys.stderr)
             return 1
-        for i, n in enumerate(names):
-            chunk = [disp[k] for k in ids[i * per + warmup:(i + 1) * per]]
+        for i, (v, _, _) in enumerate(order):
+            chunk = disp[i * per + warmup:(i + 1) * per]
             for c in chunk[0]:
-                table[n][c] = sum(x[c] for x in chunk) / len(chunk)
-    print("| variant | MFMA busy | LDS bank conflicts | HBM read KiB | HBM write KiB | what changes |")
-    print("|---|---|---|---|---|---|")
-    for n in names:
-        t = table[n]
-        busy = (t["SQ_VALU_MFMA_BUSY_CYCLES"] / (t["GRBM_GUI_ACTIVE"] / 8 * 1024)
-                if "SQ_VALU_MFMA_BUSY_CYCLES" in t and "GRBM_GUI_ACTIVE" in t else None)
-        conf = (t["SQ_LDS_BANK_CONFLICT"] / t["SQ_LDS_IDX_ACTIVE"]
-                if t.get("SQ_LDS_IDX_ACTIVE") else None)
-        cell = lambda v, f: (f % v) if v is not None else "-"
-        print("| `%s` | %s | %s | %s | %s | %s |" % (
-            n, cell(None if busy is None else 100 * busy, "%.1f%%"), cell(None if conf is None else 100 * conf, "%.1f%%"),
-            cell(t.get("FETCH_SIZE"), "%.0f"), cell(t.get("WRITE_SIZE"), "%.0f"), RUNGS.get(n, "")))
+                table[v][c] = statistics.median(x[c] for x in chunk)
+    timed = {}
+    if times:
+        with open(times) as f:
+            timed = {r["variant"]: r for r in json.loads(f.read().strip().splitlines()[-1])["rows"]}
+    mfmas = w.flops / 16384  # 16x16x32 MFMAs the product needs
+    fmt = lambda x, f: "-" if x is None else f % x
+    print("| rung | variant | TFLOP/s | % of peak | clock MHz | MFMA busy | waves waiting | "
+          "LDS instr / MFMA | SALU / MFMA | LDS bank conflicts | read beyond L2 GB | written GB | "
+          "L2 hit | what changes |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for v, rung, what in order:
+        t = table[v]
+        cyc = t.get("GRBM_GUI_ACTIVE", 0) / 8
+        clock = cyc / (t["ns"] * 1e-9) / 1e6 if cyc else None
+        busy = 100 * t["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024) if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in t else None
+        wait = 100 * t["SQ_WAIT_ANY"] / t["SQ_WAVE_CYCLES"] if t.get("SQ_WAVE_CYCLES") else None
+        lds = t["SQ_INSTS_LDS"] / mfmas if "SQ_INSTS_LDS" in t else None
+        salu = t["SQ_INSTS_SALU"] / mfmas if "SQ_INSTS_SALU" in t else None
+        conf = 100 * t["SQ_LDS_BANK_CONFLICT"] / t["SQ_LDS_IDX_ACTIVE"] if t.get("SQ_LDS_IDX_ACTIVE") else None
+        rd = 32 * t["TCC_EA0_RDREQ_DRAM_32B_sum"] / 1e9 if "TCC_EA0_RDREQ_DRAM_32B_sum" in t else None
+        wr = (64 * t["TCC_EA0_WRREQ_64B_sum"] + 32 * (t["TCC_EA0_WRREQ_sum"] - t["TCC_EA0_WRREQ_64B_sum"])) / 1e9 \
+            if "TCC_EA0_WRREQ_sum" in t else None
+        hit = 100 * t["TCC_HIT_sum"] / t["TCC_REQ_sum"] if t.get("TCC_REQ_sum") and "TCC_HIT_sum" in t else None
+        tf = timed.get(v, {}).get("tflops")
+        print("| %s | `%s` | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            rung, v, fmt(tf, "%.1f"), fmt(None if tf is None else 100 * tf / 2516.5824, "%.1f"),
+            fmt(clock, "%.0f"), fmt(busy, "%.1f%%"), fmt(wait, "%.1f%%"), fmt(lds, "%.3f"), fmt(salu, "%.3f"),
+            fmt(conf, "%.2f%%"), fmt(rd, "%.3f"), fmt(wr, "%.3f"), fmt(hit, "%.1f%%"), what))
     return 0
 
 
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--workload", default="square_8192")
-    p.add_argument("--launches", type=int, default=10)
+    p.add_argument("--settle", type=float, default=0.5, help="seconds of untimed launches before each row")
+    p.add_argument("--launches", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--cooldown", type=float, default=1.0)
-    p.add_argument("--with-simple", action="store_true", help="include the per-element kernel (slow)")
     p.add_argument("--summarize", nargs="+", metavar="DIR", help="summarise rocprofv3 counter output")
+    p.add_argument("--times", help="the JSON line of a timed run, for the TFLOP/s column")
     args = p.parse_args(argv)
     if args.summarize:
-        return summarize(args.summarize, args.warmup, args.launches, args.with_simple)
+        return summarize(args.summarize, args.warmup, args.launches, args.times, args.workload)
     return run(args)
 
 
