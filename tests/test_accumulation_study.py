@@ -76,3 +76,46 @@ def test_fp16_accumulation_of_one_block_is_one_rounding():
     a, b = workloads.gaussian(40, 24, 16, seed=7)
     _, c16 = oracle.gemm_nt(a, b)
     assert np.array_equal(fp16_accumulate(a, b).view(np.uint16), c16.view(np.uint16))
+
+
+STUDY_K = (1024, 4096, 8192, 16384)
+
+
+def accumulation_table(ks=STUDY_K, m=96, n=96):
+    """Error against the exact sum for fp16 accumulation (blocks of 16) and
+    for fp32 accumulation with one final fp16 cast, at unit-variance outputs
+    for each K (inputs N(0, K**-0.5) as in every workload): one row per K
+    with the mean, p99 and max of |error|."""
+    rows = []
+    for K in ks:
+        a, b = workloads.gaussian(m, n, K, seed=workloads.SEED_BASE + K)
+        c64, c16 = oracle.gemm_nt(a, b)
+        e16 = np.abs(fp16_accumulate(a, b).astype(np.float64) - c64)
+        e32 = np.abs(c16.astype(np.float64) - c64)
+        rows.append({"K": K,
+                     "fp16_acc": (float(e16.mean()), float(np.percentile(e16, 99)), float(e16.max())),
+                     "fp32_acc": (float(e32.mean()), float(np.percentile(e32, 99)), float(e32.max()))})
+    return rows
+
+
+def test_accumulation_error_across_k():
+    """fp16 accumulation rounds a running sum of size ~1 once per block of
+    16 products, so its error grows with the number of blocks, K / 16 (as a
+    random walk of roundings, roughly with its square root); fp32
+    accumulation leaves only the final cast, whose error does not depend on
+    K.  At K = 8192 both match the pages' figures."""
+    rows = accumulation_table()
+    print("\n    K | fp16 accumulation mean / p99 / max | fp32 accumulation, one fp16 cast: mean / p99 / max")
+    for r in rows:
+        print("%5d | %.5f / %.5f / %.4f | %.6f / %.6f / %.5f" % ((r["K"],) + r["fp16_acc"] + r["fp32_acc"]))
+    means16 = [r["fp16_acc"][0] for r in rows]
+    assert all(x < y for x, y in zip(means16, means16[1:]))
+    # a random walk of K / 16 roundings: the mean grows by about sqrt(2) per doubling of K
+    assert 2.5 < means16[-1] / means16[0] < 6.0  # 16x the blocks
+    for r in rows:
+        mean32, _, max32 = r["fp32_acc"]
+        assert 1.1e-4 < mean32 < 1.7e-4 and max32 <= 2.0e-3
+        assert r["fp16_acc"][0] > 5 * mean32
+    fig = _figures()["fp16_accumulation_vs_fp32_library"]
+    at8192 = [r for r in rows if r["K"] == 8192][0]
+    assert abs(at8192["fp16_acc"][0] - fig["mean_abs"]) < 0.2 * fig["mean_abs"]
