@@ -42,11 +42,32 @@ if ROOT not in sys.path:
 METRIC = "TFLOP/s fp16 GEMM C=A·Bᵀ at M=N=K=8192; % of MI355X dense fp16 MFMA peak"
 # 256 CUs x 4096 dense fp16 flop per clock per CU x 2.4 GHz (AMD's 2.5 PFLOP/s)
 PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
-# HBM bytes per launch measured with rocprofv3 (FETCH_SIZE x 2.000 plus
-# WRITE_SIZE x 1.000, the factors read off a plain 1 GiB device copy) for one
-# kernel on one workload.  Reported only for that pair; reset to None when the
-# kernel changes.
-TRAFFIC = {"workload": "square_8192", "kernel": "mfma16_256x256x64_w8_r5_l4_persistent", "bytes": 1.799e9}
+# Bytes per launch between the L2s and the memory controller, from two
+# rocprofv3 --pmc runs of this benchmark: FETCH_SIZE x 2.000 + WRITE_SIZE x
+# 1.000 (KiB per dispatch), the factors read off a plain 1 GiB device copy in
+# the same process; TCC_EA0_RDREQ_DRAM_32B and TCC_EA0_WRREQ_64B give the same
+# bytes.  The memory-side cache sits behind that point, so this bounds HBM
+# traffic from above.  Valid only for the kernel source it was measured on
+# (source_digest: comments and whitespace aside): null once that changes.
+TRAFFIC = {"workload": "square_8192", "kernel": "mfma16_256x256x64_w8_r5_l4_persistent", "bytes": 1.782e9,
+           "source_sha256_16": "d61b41ee1a385726"}
+SOURCE = os.path.join(ROOT, "dense_fp16_gemm_04_amd", "csrc", "gemm_nt_f16.hip")
+
+
+def source_digest() -> str:
+    """SHA-256 (16 hex digits) of the kernel source's code: comments removed
+    and whitespace collapsed, so an edit to a comment keeps the record."""
+    import hashlib
+    import re
+    try:
+        with open(SOURCE, encoding="utf-8") as f:
+            text = f.read()
+    except OSError:
+        return ""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def log(*a):
@@ -423,7 +444,8 @@ def measure(args, sampler) -> int:
         "unit": "TFLOP/s",
         "frac": tflops / PEAK_TFLOPS,
         "traffic": (TRAFFIC["bytes"] if TRAFFIC and TRAFFIC["workload"] == w.name
-                    and TRAFFIC["kernel"] == vname and rows == w.M else None),
+                    and TRAFFIC["kernel"] == vname and rows == w.M
+                    and TRAFFIC["source_sha256_16"] == source_digest() else None),
     }
     rec = {
         "metric": METRIC,

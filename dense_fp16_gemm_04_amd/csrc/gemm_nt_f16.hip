@@ -278,6 +278,14 @@ __device__ __forceinline__ void mfma16_agpr(float4_t& acc, const half8_t& b, con
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a) : "memory");
 }
 
+// acc += b * a with the accumulator held in VGPRs instead (a ladder
+// option of the persistent kernel: the epilogue then converts it without
+// moving it out of AGPRs first).
+__device__ __forceinline__ void mfma16_vgpr(float4_t& acc, const half8_t& b, const half8_t& a)
+{
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(b), "v"(a) : "memory");
+}
+
 // Store mode of C, passed to the kernels as `c_vec`: which stores the rows
 // allow (2: aligned 16-byte, 1: aligned 8-byte, 0: single elements).
 
@@ -809,15 +817,21 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
         else
             fa[set][idx - T::FN] = *(const half8_t*)(pa + (idx - T::FN) * T::MI * T::ROW_BYTES);
     };
-    // MFMAs of sub-step `cs` (block row i = t / FN, column j = t % FN), with
-    // the reads of sub-step 1 - cs from (ra_base, rb_base) and, if LD, loads
-    // [l0, l0 + LOADS_SUB) of step `lstep` into `where` interleaved.
+    // MFMAs of sub-step `cs`, along the rows of blocks and back (block row
+    // i = t / FN; column j = t % FN on even rows, FN - 1 - t % FN on odd
+    // ones), so consecutive MFMAs always share a fragment: 0.1-0.7% faster
+    // than starting every row at column 0, in alternating replays on six
+    // shapes (the clock is power-limited, and an operand that does not
+    // change costs less), with the reads of sub-step 1 - cs from (ra_base,
+    // rb_base) and, if LD, loads [l0, l0 + LOADS_SUB) of step `lstep` into
+    // `where` interleaved.
     auto substep = [&](int cs, const unsigned char* ra_base, const unsigned char* rb_base, auto ld, int where,
                        int lstep, int l0, auto masked) __attribute__((always_inline)) {
         constexpr bool LD = decltype(ld)::value;
 #pragma unroll
         for (int t = 0; t < G; ++t) {
-            mfma16_agpr(acc[t / T::FN][t % T::FN], fb[cs][t % T::FN], fa[cs][t / T::FN]);
+            const int i = t / T::FN, j = (i & 1) ? T::FN - 1 - t % T::FN : t % T::FN;
+            mfma16_agpr(acc[i][j], fb[cs][j], fa[cs][i]);
             if (t % RS == 0 && t / RS < R) read_one(1 - cs, ra_base, rb_base, t / RS);
             if constexpr (LD)
                 if (t % LS == LS / 2 && t / LS < LOADS_SUB) issue_load(where, lstep, l0 + t / LS, masked);
@@ -924,7 +938,11 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
 // pieces, four consecutive columns of one row per lane, the way "6. Four
 // Consumers, FP16 Accumulation, and a TMA Epilogue" ("Serialized
 // Shared-Memory Epilogue") describes stores straight from registers.
-template <class T, int RS, int LS, bool DIRECT = false>
+// Two more options, FLAGS bits for the ladder: kVgprAcc keeps the
+// accumulators in VGPRs, kColumns walks every column of MFMA blocks top to
+// bottom instead of every second one bottom to top.
+constexpr int kDirect = 1, kVgprAcc = 2, kColumns = 4;
+template <class T, int RS, int LS, int FLAGS = 0>
 __global__ void __launch_bounds__(T::THREADS, 1)
 gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                             _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
@@ -936,6 +954,7 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
                   "waves that all load");
     // with eight waves the four that never load store C; with four, all do
     constexpr bool ALL_STORE = T::WAVES == T::LOADERS;
+    constexpr bool DIRECT = FLAGS & kDirect, VACC = FLAGS & kVgprAcc, SNAKE = !(FLAGS & kColumns);
     constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
     constexpr int R = T::FM + T::FN;  // fragment reads per sub-step
     constexpr int SLOT = T::A_BYTES;  // one operand tile of one step
@@ -1025,7 +1044,10 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
         return z;
     };
     auto clear = [&](int i, int j, const half8_t& z) __attribute__((always_inline)) {
-        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %1, 0" : "=a"(acc[i][j]) : "v"(z) : "memory");
+        if constexpr (VACC)
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %1, 0" : "=v"(acc[i][j]) : "v"(z) : "memory");
+        else
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %1, 0" : "=a"(acc[i][j]) : "v"(z) : "memory");
     };
 
     // fragment read `idx` of set `set`, in the order the MFMAs below first
@@ -1043,10 +1065,14 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
     };
     // MFMAs of sub-step cs, with (if RD) the fragment reads of sub-step 1 -
     // cs and (if LD) loads l0 .. l0 + A_LOADS - 1 of step lstep interleaved.
-    // The MFMAs go down the columns of blocks (block row i = t % FM, column
-    // j = t / FM), so each run of FM of them shares one B fragment; that
-    // order ran 0.3-1.1% faster than along the rows (runs of FN sharing an A
-    // fragment) in alternating replays at 8192^3 and 4096 x 4096 x 16384.
+    // The MFMAs go down the columns of blocks (column j = t / FM) and, unless
+    // kColumns, back up every second one (block row i = t % FM, or FM - 1 -
+    // t % FM on odd columns): each run of FM shares one B fragment, and the
+    // turn at the end of a column keeps the A fragment.  Columns ran 0.3-1.1%
+    // faster than rows (runs of FN sharing an A fragment), and the turns
+    // another 0.4-0.5%, in alternating replays at 8192^3, 4096^3 and 4096 x
+    // 4096 x 16384: the clock is power-limited, and an operand that does not
+    // change between MFMAs costs less.
     auto substep = [&](int cs, const unsigned char* ra_base, const unsigned char* rb_base, auto ld, int where,
                        int lstep, int l0, auto masked, auto rd) __attribute__((always_inline)) {
         constexpr bool LD = decltype(ld)::value, RD = decltype(rd)::value;
@@ -1054,7 +1080,11 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
         asm volatile("" : "+s"(rbytes));
 #pragma unroll
         for (int t = 0; t < G; ++t) {
-            mfma16_agpr(acc[t % T::FM][t / T::FM], fb[cs][t / T::FM], fa[cs][t % T::FM]);
+            const int j = t / T::FM, i = SNAKE && (j & 1) ? T::FM - 1 - t % T::FM : t % T::FM;
+            if constexpr (VACC)
+                mfma16_vgpr(acc[i][j], fb[cs][j], fa[cs][i]);
+            else
+                mfma16_agpr(acc[i][j], fb[cs][j], fa[cs][i]);
             if constexpr (RD)
                 if (t % RS == 0 && t / RS < R) read_one(1 - cs, ra_base, rb_base, t / RS);
             if constexpr (LD)
@@ -1364,7 +1394,8 @@ int launch_ordered(const void* A, const void* B, void* C, int64_t M, int64_t N, 
     const int64_t tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > kMaxMN) return hipErrorInvalidValue;
     const int c_vec = c_store_mode(N, C);
-    hipLaunchKernelGGL((gemm_nt_f16_ordered<T, RS, LS, SLOTS5>), dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_nt_f16_ordered<T, RS, LS, SLOTS5>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(T::THREADS), 0,
                        stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N, (int)K,
                        (int)tiles_m, (int)tiles_n, group_m, c_vec);
     return (int)hipGetLastError();
@@ -1374,7 +1405,7 @@ int launch_ordered(const void* A, const void* B, void* C, int64_t M, int64_t N, 
 // where its conditions hold, else the one-tile-per-workgroup 5-slot kernel.
 // Its epilogue is faster than the other's even with one tile per workgroup
 // (4096^3: +1%).
-template <class T, int RS, int LS, bool DIRECT = false>
+template <class T, int RS, int LS, int FLAGS = 0>
 int launch_ordered_persist(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int group_m,
                            hipStream_t stream)
 {
@@ -1387,7 +1418,7 @@ int launch_ordered_persist(const void* A, const void* B, void* C, int64_t M, int
     // (C offsets are 32-bit and columns past N are sent to kOob: N <= 2^22)
     if ((c_vec & 3) != 2 || K <= T::BK || N > (int64_t(1) << 22))
         return launch_ordered<T, RS, LS, true>(A, B, C, M, N, K, group_m, stream);
-    hipLaunchKernelGGL((gemm_nt_f16_ordered_persist<T, RS, LS, DIRECT>), dim3((unsigned)grid), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_nt_f16_ordered_persist<T, RS, LS, FLAGS>), dim3((unsigned)grid), dim3(T::THREADS), 0,
                        stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N, (int)K,
                        (int)tiles_m, (int)tiles_n, group_m, c_vec);
     return (int)hipGetLastError();
@@ -1442,7 +1473,12 @@ constexpr Variant kVariants[] = {
     {"mfma16_256x256x64_w8_r5_l4_persistent_group4", 256, 256, 4, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2>},
     {"mfma16_256x256x64_w8_r5_l4_persistent_noxcd", 256, 256, -8, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2>},
     {"mfma16_256x256x64_w8_r5_l4_persistent_linear", 256, 256, 0, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2>},
-    {"mfma16_256x256x64_w8_r5_l4_persistent_direct", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2, true>},
+    {"mfma16_256x256x64_w8_r5_l4_persistent_direct", 256, 256, 8,
+     launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2, kDirect>},
+    {"mfma16_256x256x64_w8_r5_l4_persistent_vacc", 256, 256, 8,
+     launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2, kVgprAcc>},
+    {"mfma16_256x256x64_w8_r5_l4_persistent_columns", 256, 256, 8,
+     launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2, kColumns>},
     {"mfma16_256x256x64_w4_r5_persistent", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 4, 8>},
     {"mfma16_256x256x64_w4_r5_persistent_rs2", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8>},
     {"mfma16_256x256x64_w4_r5_persistent_rs3", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 3, 8>},

@@ -36,13 +36,15 @@ script fixes: every row gets warmup + launches dispatches, in table order,
 and nothing else launches a kernel whose name contains gemm_nt_f16.
 
 Counter readings (GRBM_GUI_ACTIVE counts cycles on each of the 8 XCDs; the
-matrix-core busy cycles, per SIMD, are over 1024 SIMDs): clock =
-GRBM_GUI_ACTIVE / 8 / kernel time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
-(GRBM_GUI_ACTIVE / 8 * 1024); bytes read beyond L2 =
-32 * TCC_EA0_RDREQ_DRAM_32B_sum and bytes written = 64 * TCC_EA0_WRREQ_64B_sum
-+ 32 * (TCC_EA0_WRREQ_sum - TCC_EA0_WRREQ_64B_sum), factors read off a plain
-1 GiB device copy, which these counters report as exactly 1 GiB read and
-1 GiB written.  The memory-side cache (MALL) sits behind that point, so
+matrix-core busy cycles, per SIMD, are over 1024 SIMDs): MFMA busy =
+SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 * 1024), a fraction of
+cycles whatever the clock; the implied clock is the one at which the timed
+rate and that fraction agree, TFLOP/s / (busy * 1048.576 TFLOP/s per GHz)
+(counted dispatches run one at a time, not at the sustained clock);
+bytes read beyond L2 = 32 * TCC_EA0_RDREQ_DRAM_32B_sum and bytes written =
+64 * TCC_EA0_WRREQ_64B_sum + 32 * (TCC_EA0_WRREQ_sum - TCC_EA0_WRREQ_64B_sum),
+factors read off a plain 1 GiB device copy, which these counters report as
+exactly 1 GiB read and 1 GiB written.  The memory-side cache (MALL) sits behind that point, so
 these are requests that leave the L2s for the memory controller: an upper
 bound on HBM traffic.
 """
@@ -65,9 +67,9 @@ if ROOT not in sys.path:
 LADDER = [
     ("simple_f32_per_element", "R0",
      "one thread per output, fp32 FMAs from global memory: no tiling, no matrix cores"),
-    ("mfma16_128x128x64_w4_s1", "R1",
-     "128x128 tiles in LDS, 4 waves of 16x16x32 MFMAs; one stage: load, wait, compute "
-     "(V0: the copy runs, then everyone waits)"),
+    ("mfma16_128x128x64_w4_s1_one_per_cu", "R1",
+     "128x128 tiles in LDS, 4 waves of 16x16x32 MFMAs, one workgroup per CU; one stage: "
+     "load, wait, compute (V0: the copy runs, then everyone waits)"),
     ("mfma16_128x128x64_w4_s3", "R2",
      "3-stage ring: the loads of later steps overlap the MFMAs (V2's multi-stage ring)"),
     ("mfma16_128x128x64_w8_s3_l4_ordered", "R3",
@@ -84,8 +86,12 @@ LADDER = [
      "under this tile's last steps, C staged through LDS (the default)"),
 ]
 
-# (variant, what differs from the default kernel, R7)
+# (variant, what differs: from R1 for the first row, else from the default
+# kernel, R7)
 SIDE = [
+    ("mfma16_128x128x64_w4_s1",
+     "R1 without the one-workgroup limit: its 32 KiB of LDS lets four workgroups share a CU, "
+     "and they overlap each other's copies and MFMAs (CDNA4's way to hide a load without a ring)"),
     ("mfma16_256x256x64_w8_r5_l4_persistent_direct",
      "C stored straight from registers as 8-byte pieces, no LDS staging "
      "(V6's 'Serialized Shared-Memory Epilogue', undone)"),
@@ -95,6 +101,11 @@ SIDE = [
      "the pages' grouped raster (8 rows) without renumbering tiles per XCD"),
     ("mfma16_256x256x64_w8_r5_l4_persistent_linear",
      "tiles in row-major order: no grouped raster, no XCD renumbering"),
+    ("mfma16_256x256x64_w8_r5_l4_persistent_columns",
+     "MFMAs down every column of blocks top to bottom, not back up every second one: at each "
+     "column's end both fragments change"),
+    ("mfma16_256x256x64_w8_r5_l4_persistent_vacc",
+     "accumulators in VGPRs instead of AGPRs (the epilogue converts them without moving them first)"),
     ("mfma16_256x256x64_w4_r5_persistent",
      "4 waves of 128x128 (one per SIMD, accumulators in all 256 AGPRs): "
      "a third fewer LDS reads per MFMA"),
@@ -199,14 +210,13 @@ def summarize(dirs, warmup, launches, times=None, workload="square_8192") -> int
             timed = {r["variant"]: r for r in json.loads(f.read().strip().splitlines()[-1])["rows"]}
     mfmas = w.flops / 16384  # 16x16x32 MFMAs the product needs
     fmt = lambda x, f: "-" if x is None else f % x
-    print("| rung | variant | TFLOP/s | % of peak | clock MHz | MFMA busy | waves waiting | "
+    print("| rung | variant | TFLOP/s | % of peak | MFMA busy | implied clock MHz | waves waiting | "
           "LDS instr / MFMA | SALU / MFMA | LDS bank conflicts | read beyond L2 GB | written GB | "
           "L2 hit | what changes |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for v, rung, what in order:
         t = table[v]
         cyc = t.get("GRBM_GUI_ACTIVE", 0) / 8
-        clock = cyc / (t["ns"] * 1e-9) / 1e6 if cyc else None
         busy = 100 * t["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024) if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in t else None
         wait = 100 * t["SQ_WAIT_ANY"] / t["SQ_WAVE_CYCLES"] if t.get("SQ_WAVE_CYCLES") else None
         lds = t["SQ_INSTS_LDS"] / mfmas if "SQ_INSTS_LDS" in t else None
@@ -217,9 +227,12 @@ def summarize(dirs, warmup, launches, times=None, workload="square_8192") -> int
             if "TCC_EA0_WRREQ_sum" in t else None
         hit = 100 * t["TCC_HIT_sum"] / t["TCC_REQ_sum"] if t.get("TCC_REQ_sum") and "TCC_HIT_sum" in t else None
         tf = timed.get(v, {}).get("tflops")
+        # the clock at which the timed rate and the counted busy fraction
+        # agree: TFLOP/s = busy * 1024 SIMDs * 1024 flop/clock * clock
+        implied = tf / (busy / 100 * 1.048576) if tf and busy else None
         print("| %s | `%s` | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
             rung, v, fmt(tf, "%.1f"), fmt(None if tf is None else 100 * tf / 2516.5824, "%.1f"),
-            fmt(clock, "%.0f"), fmt(busy, "%.1f%%"), fmt(wait, "%.1f%%"), fmt(lds, "%.3f"), fmt(salu, "%.3f"),
+            fmt(busy, "%.1f%%"), fmt(implied, "%.0f"), fmt(wait, "%.1f%%"), fmt(lds, "%.3f"), fmt(salu, "%.3f"),
             fmt(conf, "%.2f%%"), fmt(rd, "%.3f"), fmt(wr, "%.3f"), fmt(hit, "%.1f%%"), what))
     return 0
 

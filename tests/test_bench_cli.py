@@ -112,3 +112,20 @@ def test_cpu_configs_table(monkeypatch):
     assert [(r["workload"], r["threads"]) for r in t["runs"]] == [
         (w.name, th) for w in small for th in ([t["threads"], 1])]
     assert all(r["seconds"] > 0 and r["gflops"] > 0 for r in t["runs"])
+
+
+def test_traffic_record_follows_the_kernel_code_not_its_comments(tmp_path, monkeypatch):
+    """bench.py reports the measured traffic only for the kernel code it was
+    measured on: the digest ignores comments and whitespace, and changes with
+    any code."""
+    import bench
+
+    src = tmp_path / "k.hip"
+    src.write_text("// a comment\nint f(int x) { return x + 1; }  /* more */\n")
+    monkeypatch.setattr(bench, "SOURCE", str(src))
+    d0 = bench.source_digest()
+    src.write_text("// another comment\nint f(int x)\n{\n    return x + 1;\n}\n")
+    assert bench.source_digest() == d0
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.source_digest() != d0
+    assert len(d0) == 16
