@@ -940,8 +940,11 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
 // Shared-Memory Epilogue") describes stores straight from registers.
 // Two more options, FLAGS bits for the ladder: kVgprAcc keeps the
 // accumulators in VGPRs, kColumns walks every column of MFMA blocks top to
-// bottom instead of every second one bottom to top.
-constexpr int kDirect = 1, kVgprAcc = 2, kColumns = 4;
+// bottom instead of every second one bottom to top.  kSharedM0: groups of
+// four global->LDS loads share one LDS base (M0), the pieces placed by the
+// instruction offset; every load that needs a new M0 value costs the wave
+// several issue cycles.
+constexpr int kDirect = 1, kVgprAcc = 2, kColumns = 4, kSharedM0 = 8;
 template <class T, int RS, int LS, int FLAGS = 0>
 __global__ void __launch_bounds__(T::THREADS, 1)
 gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
@@ -954,7 +957,10 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
                   "waves that all load");
     // with eight waves the four that never load store C; with four, all do
     constexpr bool ALL_STORE = T::WAVES == T::LOADERS;
-    constexpr bool DIRECT = FLAGS & kDirect, VACC = FLAGS & kVgprAcc, SNAKE = !(FLAGS & kColumns);
+    constexpr bool DIRECT = FLAGS & kDirect, VACC = FLAGS & kVgprAcc, SNAKE = !(FLAGS & kColumns),
+                   SHARED_M0 = FLAGS & kSharedM0;
+    static_assert(!SHARED_M0 || (T::A_LOADS % 4 == 0 && T::B_LOADS % 4 == 0),
+                  "loads come in groups of four pieces");
     constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
     constexpr int R = T::FM + T::FN;  // fragment reads per sub-step
     constexpr int SLOT = T::A_BYTES;  // one operand tile of one step
@@ -1011,11 +1017,36 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
         const uint32_t off = (uint32_t)(g * T::ROWS_PER_LOAD) * rbytes + vpar[l & 1];
         const uint32_t v = (!MASKED || kpar[l & 1] < K - k0) ? off : kOob;
         const uint32_t soff = (uint32_t)k0 * 2u;
-        unsigned char* dst = smem + where * SLOT + g * 1024;
-        if (l < T::A_LOADS)  // (a buffer resource cannot be the result of ?:)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(la, (lds_void_t*)dst, 16, v, soff, 0, 0);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(lb, (lds_void_t*)dst, 16, v, soff, 0, 0);
+        if constexpr (SHARED_M0) {
+            // Load r = g % 4 of a group of four consecutive 1 KiB pieces: the
+            // LDS destination is the group's first piece (one M0 value for all
+            // four) plus the instruction offset r KiB, which the hardware also
+            // adds to the global offset, so the VGPR offset gives it back.
+            // No wrap: the row offset of piece g >= r is at least g * 8 rows
+            // * 2K bytes >= r KiB for K >= 64 (this kernel runs K > 64), and
+            // the out-of-range sentinel stays past every tile's buffer.
+            const int r = g & 3;
+            lds_void_t* dst = (lds_void_t*)(smem + where * SLOT + (g - r) * 1024);
+            const uint32_t vr = v - (uint32_t)r * 1024u;
+            auto load = [&](__amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
+                switch (r) {  // (the instruction offset must be a constant)
+                    case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vr, soff, 0, 0); break;
+                    case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vr, soff, 1024, 0); break;
+                    case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vr, soff, 2048, 0); break;
+                    default: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vr, soff, 3072, 0); break;
+                }
+            };
+            if (l < T::A_LOADS)  // (a buffer resource cannot be the result of ?:)
+                load(la);
+            else
+                load(lb);
+        } else {
+            unsigned char* dst = smem + where * SLOT + g * 1024;
+            if (l < T::A_LOADS)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(la, (lds_void_t*)dst, 16, v, soff, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(lb, (lds_void_t*)dst, 16, v, soff, 0, 0);
+        }
     };
 
     const int fr_row = lane % T::MI;
@@ -1479,11 +1510,10 @@ constexpr Variant kVariants[] = {
      launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2, kVgprAcc>},
     {"mfma16_256x256x64_w8_r5_l4_persistent_columns", 256, 256, 8,
      launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2, kColumns>},
+    {"mfma16_256x256x64_w4_r5_persistent_rs2_m0", 256, 256, 8,
+     launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8, kSharedM0>},
     {"mfma16_256x256x64_w4_r5_persistent", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 4, 8>},
     {"mfma16_256x256x64_w4_r5_persistent_rs2", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8>},
-    {"mfma16_256x256x64_w4_r5_persistent_rs3", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 3, 8>},
-    {"mfma16_256x256x64_w4_r5_persistent_rs1", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 1, 8>},
-    {"mfma16_256x256x64_w4_r5_persistent_rs2_ls6", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 6>},
     {"mfma16_256x128x64_w8_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_256x128x64_w8x_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 4, 2, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_128x128x64_w8_s3_l4_ordered", 128, 128, 8, launch_ordered<TileShape<128, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},

@@ -106,9 +106,11 @@ SIDE = [
      "column's end both fragments change"),
     ("mfma16_256x256x64_w8_r5_l4_persistent_vacc",
      "accumulators in VGPRs instead of AGPRs (the epilogue converts them without moving them first)"),
-    ("mfma16_256x256x64_w4_r5_persistent",
-     "4 waves of 128x128 (one per SIMD, accumulators in all 256 AGPRs): "
-     "a third fewer LDS reads per MFMA"),
+    ("mfma16_256x256x64_w4_r5_persistent_rs2",
+     "4 waves of 128x128 (one per SIMD, accumulators in all 256 AGPRs): a third fewer LDS "
+     "reads per MFMA; fragment reads over the first half of each sub-step"),
+    ("mfma16_256x256x64_w4_r5_persistent_rs2_m0",
+     "the same, with each group of four global->LDS loads sharing one LDS base (M0)"),
     ("mfma16_256x256x64_w8_s2",
      "compiler-scheduled 256x256, 8 waves, all loading, 2-stage ring (16x16x32 MFMAs)"),
     ("mfma32_256x256x64_w8_s2",
