@@ -944,7 +944,19 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
 // four global->LDS loads share one LDS base (M0), the pieces placed by the
 // instruction offset; every load that needs a new M0 value costs the wave
 // several issue cycles.
-constexpr int kDirect = 1, kVgprAcc = 2, kColumns = 4, kSharedM0 = 8;
+// kLean (four waves only) strips the scalar and vector arithmetic out of the
+// steps that load whole K ranges.  With one wave per SIMD nothing hides that
+// arithmetic: between two MFMAs (16 cycles of the matrix core) a lone wave
+// issues one scalar instruction for free, and each further one delays the
+// next MFMA by about 8 cycles (a vector one by about 5).  Such steps run as a
+// cycle of five, one per position of the slot ring, so every slot offset is
+// a constant; the fragment reads use per-lane base addresses kept in
+// registers (three copies 64 KiB apart, so that every offset fits the read's
+// 16-bit immediate), the loads keep their per-lane offsets in registers and
+// share M0 in groups of four, and the K position advances in one scalar
+// register.  Steps past the end of K and the two steps that start the next
+// tile keep the general form.
+constexpr int kDirect = 1, kVgprAcc = 2, kColumns = 4, kSharedM0 = 8, kLean = 16;
 template <class T, int RS, int LS, int FLAGS = 0>
 __global__ void __launch_bounds__(T::THREADS, 1)
 gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
@@ -958,7 +970,10 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
     // with eight waves the four that never load store C; with four, all do
     constexpr bool ALL_STORE = T::WAVES == T::LOADERS;
     constexpr bool DIRECT = FLAGS & kDirect, VACC = FLAGS & kVgprAcc, SNAKE = !(FLAGS & kColumns),
-                   SHARED_M0 = FLAGS & kSharedM0;
+                   SHARED_M0 = FLAGS & kSharedM0, LEAN = FLAGS & kLean;
+    static_assert(!LEAN || (ALL_STORE && !DIRECT && !VACC && T::A_LOADS == 8 && T::B_LOADS == 8 &&
+                            T::A_BYTES == 32768 && T::KK == 2),
+                  "the lean steps: four waves, 32 KiB slots, 8 + 8 loads per wave and step");
     static_assert(!SHARED_M0 || (T::A_LOADS % 4 == 0 && T::B_LOADS % 4 == 0),
                   "loads come in groups of four pieces");
     constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
@@ -1057,6 +1072,30 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, T::CPS * kk + fr_hi) * 16;
 
+    // LEAN: rdb[c][x][kk] is this lane's LDS address of operand x's (A, B)
+    // fragment rows at k-half kk, plus c * 64 KiB (slots 2c and 2c + 1 are
+    // reached with an immediate of 0 or 32 KiB); lvo[l] the VGPR offset of
+    // load l of this wave (A and B loads l and l + 8 fill the same rows of
+    // their tiles), less the instruction offset that places it within its
+    // group of four (see issue_load).
+    uint32_t rdb[LEAN ? 3 : 1][2][T::KK];
+    uint32_t lvo[LEAN ? 8 : 1];
+    if constexpr (LEAN) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+#pragma unroll
+            for (int kk = 0; kk < T::KK; ++kk) {
+                rdb[c][0][kk] = (uint32_t)(c * 65536 + a_row0 * T::ROW_BYTES + fr_pos[kk]);
+                rdb[c][1][kk] = (uint32_t)(c * 65536 + b_row0 * T::ROW_BYTES + fr_pos[kk]);
+                asm volatile("" : "+v"(rdb[c][0][kk]), "+v"(rdb[c][1][kk]));
+            }
+#pragma unroll
+        for (int l = 0; l < 8; ++l) {
+            lvo[l] = (uint32_t)((lw * 8 + l) * T::ROWS_PER_LOAD) * row_bytes + vpar[l & 1] - (uint32_t)(l & 3) * 1024u;
+            asm volatile("" : "+v"(lvo[l]));
+        }
+    }
+
     half8_t fa[2][T::FM], fb[2][T::FN];
     typename T::acc_t acc[T::FM][T::FN];
     // Accumulators are cleared in place by an MFMA of zero fragments with an
@@ -1121,6 +1160,71 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
             if constexpr (LD)
                 if (t % LS == LS / 2 && t / LS < T::A_LOADS) issue_load(where, lstep, l0 + t / LS, masked, rbytes);
         }
+    };
+
+    // LEAN steps.  Fragment read idx of set `set` from the A tile in slot SA
+    // and the B tile in slot SB (order as in read_one).
+    auto read_fast = [&](auto sa_c, auto sb_c, int set, int idx) __attribute__((always_inline)) {
+        constexpr int SA = decltype(sa_c)::value, SB = decltype(sb_c)::value;
+        if (idx == 0)
+            fb[set][0] = *(const half8_t*)(smem + rdb[SB / 2][1][set] + (SB % 2) * SLOT);
+        else if (idx <= T::FM)
+            fa[set][idx - 1] = *(const half8_t*)(smem + rdb[SA / 2][0][set] + (SA % 2) * SLOT +
+                                                 (idx - 1) * T::MI * T::ROW_BYTES);
+        else
+            fb[set][idx - T::FM] = *(const half8_t*)(smem + rdb[SB / 2][1][set] + (SB % 2) * SLOT +
+                                                     (idx - T::FM) * T::MI * T::ROW_BYTES);
+    };
+    // Load l (0-7: A, 8-15: B) of the step whose K range starts soff bytes
+    // into each row, into slot WHERE: piece lw * 8 + (l & 7) of the tile, in
+    // groups of four sharing M0 (base of the group) with the instruction
+    // offset (l & 3) KiB.
+    int lw_bytes = __builtin_amdgcn_readfirstlane(lw * 8 * 1024);
+    auto load_fast = [&](auto where_c, int l, uint32_t soff) __attribute__((always_inline)) {
+        constexpr int WHERE = decltype(where_c)::value;
+        lds_void_t* dst = (lds_void_t*)(smem + WHERE * SLOT + lw_bytes + (l & 4) * 1024);
+        const uint32_t vo = lvo[l & 7];
+        auto load = [&](__amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
+            switch (l & 3) {  // (the instruction offset must be a constant)
+                case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vo, soff, 0, 0); break;
+                case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vo, soff, 1024, 0); break;
+                case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vo, soff, 2048, 0); break;
+                default: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, vo, soff, 3072, 0); break;
+            }
+        };
+        if (l < 8)  // (a buffer resource cannot be the result of ?:)
+            load(la);
+        else
+            load(lb);
+    };
+    // Sub-step cs of a lean step: its MFMAs, the other set's fragment reads
+    // from slots RA and RB, and loads l0 .. l0 + 7 into slot WHERE, placed as
+    // in substep.
+    auto substep_fast = [&](int cs, auto ra, auto rb, auto where_c, int l0, uint32_t soff)
+                            __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+            const int j = t / T::FM, i = SNAKE && (j & 1) ? T::FM - 1 - t % T::FM : t % T::FM;
+            mfma16_agpr(acc[i][j], fb[cs][j], fa[cs][i]);
+            if (t % RS == 0 && t / RS < R) read_fast(ra, rb, 1 - cs, t / RS);
+            if (t % LS == LS / 2 && t / LS < T::A_LOADS) load_fast(where_c, l0 + t / LS, soff);
+        }
+    };
+    // A lean step with the computed step's A tile in slot S (what step()
+    // does with sa == S and a whole K range to load).
+    auto step_fast = [&](auto s_c, uint32_t soff) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        // The base registers are redefined (in place, by no instruction) at
+        // every step, so the compiler cannot hoist base + offset sums out of
+        // the loop into registers of their own; each stays a read's immediate.
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+#pragma unroll
+            for (int kk = 0; kk < T::KK; ++kk) asm volatile("" : "+v"(rdb[c][0][kk]), "+v"(rdb[c][1][kk]));
+        asm volatile("" : "+s"(lw_bytes));
+        substep_fast(0, Int<S>{}, Int<(S + 1) % 5>{}, Int<(S + 4) % 5>{}, 0, soff);
+        lds_barrier<T::A_LOADS>();
+        substep_fast(1, Int<(S + 2) % 5>{}, Int<(S + 3) % 5>{}, Int<S>{}, T::A_LOADS, soff);
     };
 
     // Epilogue of the tile at (cm0, cn0) through slots s0 and s1: round h
@@ -1271,6 +1375,26 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
         auto advance = [&]() __attribute__((always_inline)) { sa = sa + 2 >= 5 ? sa - 3 : sa + 2; };
         for (;;) {
             int ks = 0;
+            if constexpr (LEAN) {
+                // general steps until the ring is back at slot 0 (at most
+                // four), then lean cycles of five steps from slot 0 (a loop
+                // with one entry: entering a cycle at any of its five steps
+                // makes the control flow irreducible, which the compiler
+                // handles badly)
+                for (; ks + 2 < nfull && sa != 0; ++ks) {
+                    step(ks + 2, Flag<false>{}, Flag<false>{});
+                    advance();
+                }
+                uint32_t soff = (uint32_t)(ks + 2) * T::ROW_BYTES;  // K range of the step loaded, in bytes
+                for (; ks + 2 + 5 <= nfull; ks += 5) {
+                    step_fast(Int<0>{}, soff);
+                    step_fast(Int<2>{}, soff + T::ROW_BYTES);
+                    step_fast(Int<4>{}, soff + 2 * T::ROW_BYTES);
+                    step_fast(Int<1>{}, soff + 3 * T::ROW_BYTES);
+                    step_fast(Int<3>{}, soff + 4 * T::ROW_BYTES);
+                    soff += 5 * T::ROW_BYTES;
+                }
+            }
             for (; ks + 2 < nfull; ++ks) {
                 step(ks + 2, Flag<false>{}, Flag<false>{});
                 advance();
@@ -1514,6 +1638,7 @@ constexpr Variant kVariants[] = {
      launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8, kSharedM0>},
     {"mfma16_256x256x64_w4_r5_persistent", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 4, 8>},
     {"mfma16_256x256x64_w4_r5_persistent_rs2", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8>},
+    {"mfma16_256x256x64_w4_r5_persistent_lean", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8, kLean>},
     {"mfma16_256x128x64_w8_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_256x128x64_w8x_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 4, 2, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_128x128x64_w8_s3_l4_ordered", 128, 128, 8, launch_ordered<TileShape<128, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},

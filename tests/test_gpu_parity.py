@@ -372,6 +372,26 @@ def test_many_tiles_per_workgroup_every_variant(M, N, K):
         assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), (M, N, K, name)
 
 
+@pytest.mark.parametrize("K", [960, 1024, 1088, 1152, 1216, 1000, 1208])
+def test_persistent_ring_positions(K):
+    """The persistent kernels rotate a five-slot ring across tiles, and the
+    lean one runs its whole-K-range steps as a cycle of five from slot 0
+    after up to four general steps.  544 tiles of 256 x 256 give every
+    workgroup two or three tiles; a tile of nk steps moves the ring by 2 nk
+    slots, so nk = 15 .. 19 (K = 960 .. 1216) starts the second tile at each
+    of the five positions, and K = 1000 and 1208 add a K tail (a last step
+    of 40 and 56 columns).  Integer inputs, bit-exact."""
+    M, N = 4352, 8192
+    a, b = workloads.small_integers(M, N, K, seed=K * 31 + 5)
+    _, c16 = oracle.gemm_nt(a, b)
+    for name, vid in variant_ids().items():
+        if "persistent" not in name:
+            continue
+        print("case ring", M, N, K, name, flush=True)
+        got = run(a, b, variant=vid)
+        assert np.array_equal(got.view(np.uint16), c16.view(np.uint16)), (M, N, K, name)
+
+
 @pytest.mark.parametrize("M,N,K", [(4200, 4352, 1024), (4104, 4096, 2048), (4352, 4360, 2048)])
 def test_split_launch_plan(M, N, K):
     """Shapes whose 256x256 tiles leave a small last wave: gemm_nt_f16 runs
