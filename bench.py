@@ -49,8 +49,8 @@ PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 # bytes.  The memory-side cache sits behind that point, so this bounds HBM
 # traffic from above.  Valid only for the kernel source it was measured on
 # (source_digest: comments and whitespace aside): null once that changes.
-TRAFFIC = {"workload": "square_8192", "kernel": "mfma16_256x256x64_w8_r5_l4_persistent", "bytes": 1.782e9,
-           "source_sha256_16": "d453049cb3b93879"}
+TRAFFIC = {"workload": "square_8192", "kernel": "mfma16_256x256x64_w4_r5_persistent_lean", "bytes": 1.818e9,
+           "source_sha256_16": "6d9812ce6da1048d"}
 SOURCE = os.path.join(ROOT, "dense_fp16_gemm_04_amd", "csrc", "gemm_nt_f16.hip")
 
 

@@ -947,8 +947,9 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
 // kLean (four waves only) strips the scalar and vector arithmetic out of the
 // steps that load whole K ranges.  With one wave per SIMD nothing hides that
 // arithmetic: between two MFMAs (16 cycles of the matrix core) a lone wave
-// issues one scalar instruction for free, and each further one delays the
-// next MFMA by about 8 cycles (a vector one by about 5).  Such steps run as a
+// issues one scalar or two vector instructions for free, and each further
+// one delays the next MFMA by about 8 cycles (scalar) or 5 (vector), as
+// measured with a probe loop of independent MFMAs.  Such steps run as a
 // cycle of five, one per position of the slot ring, so every slot offset is
 // a constant; the fragment reads use per-lane base addresses kept in
 // registers (three copies 64 KiB apart, so that every offset fits the read's
@@ -1163,17 +1164,20 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
     };
 
     // LEAN steps.  Fragment read idx of set `set` from the A tile in slot SA
-    // and the B tile in slot SB (order as in read_one).
+    // and the B tile in slot SB: B fragments 0 .. FN - 1, then A fragments
+    // FM - 1 .. 0, the order in which the other set's MFMAs (down the
+    // columns, the last column bottom to top) last used their registers.
+    // (All of them are read in the first part of the sub-step and used in
+    // the next one, so the order does not delay any MFMA; it was 0.1-0.3%
+    // faster than read_one's order.)
     auto read_fast = [&](auto sa_c, auto sb_c, int set, int idx) __attribute__((always_inline)) {
         constexpr int SA = decltype(sa_c)::value, SB = decltype(sb_c)::value;
-        if (idx == 0)
-            fb[set][0] = *(const half8_t*)(smem + rdb[SB / 2][1][set] + (SB % 2) * SLOT);
-        else if (idx <= T::FM)
-            fa[set][idx - 1] = *(const half8_t*)(smem + rdb[SA / 2][0][set] + (SA % 2) * SLOT +
-                                                 (idx - 1) * T::MI * T::ROW_BYTES);
+        if (idx < T::FN)
+            fb[set][idx] = *(const half8_t*)(smem + rdb[SB / 2][1][set] + (SB % 2) * SLOT +
+                                             idx * T::MI * T::ROW_BYTES);
         else
-            fb[set][idx - T::FM] = *(const half8_t*)(smem + rdb[SB / 2][1][set] + (SB % 2) * SLOT +
-                                                     (idx - T::FM) * T::MI * T::ROW_BYTES);
+            fa[set][R - 1 - idx] = *(const half8_t*)(smem + rdb[SA / 2][0][set] + (SA % 2) * SLOT +
+                                                     (R - 1 - idx) * T::MI * T::ROW_BYTES);
     };
     // Load l (0-7: A, 8-15: B) of the step whose K range starts soff bytes
     // into each row, into slot WHERE: piece lw * 8 + (l & 7) of the tile, in
@@ -1638,7 +1642,7 @@ constexpr Variant kVariants[] = {
      launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8, kSharedM0>},
     {"mfma16_256x256x64_w4_r5_persistent", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 4, 8>},
     {"mfma16_256x256x64_w4_r5_persistent_rs2", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8>},
-    {"mfma16_256x256x64_w4_r5_persistent_lean", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8, kLean>},
+    {"mfma16_256x256x64_w4_r5_persistent_lean", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 3, 8, kLean>},
     {"mfma16_256x128x64_w8_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_256x128x64_w8x_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 4, 2, 3, 2, 0, 4, 1, 16>, 1, 1>},
     {"mfma16_128x128x64_w8_s3_l4_ordered", 128, 128, 8, launch_ordered<TileShape<128, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
@@ -1713,12 +1717,12 @@ struct Candidate {
 };
 
 constexpr Candidate kCandidates[] = {
-    {variant_index("mfma16_256x256x64_w8_r5_l4_persistent"), 256, 256, 1500.0, 3.0},
+    {variant_index("mfma16_256x256x64_w4_r5_persistent_lean"), 256, 256, 1545.0, 3.0},
     {variant_index("mfma16_256x128x64_w8x_s3_l4_ordered"), 256, 128, 1330.0, 3.0},
     {variant_index("mfma16_128x128x64_w8_s3_l4_ordered"), 128, 128, 1150.0, 3.0},
     {variant_index("mfma16_64x64x64_w4_s3"), 64, 64, 730.0, 3.0},
 };
-static_assert(variant_index("mfma16_256x256x64_w8_r5_l4_persistent") >= 0 &&
+static_assert(variant_index("mfma16_256x256x64_w4_r5_persistent_lean") >= 0 &&
                   variant_index("mfma16_256x128x64_w8x_s3_l4_ordered") >= 0 &&
                   variant_index("mfma16_128x128x64_w8_s3_l4_ordered") >= 0 &&
                   variant_index("mfma16_64x64x64_w4_s3") >= 0,

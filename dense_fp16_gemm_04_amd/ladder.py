@@ -7,7 +7,9 @@ The pages build their kernel in steps ("0. A Minimal Hopper Matmul" through
 multi-stage ring, producer/consumer warps, a larger tile, more consumers,
 a grouped tile raster and a staged epilogue.  The rungs below take the same
 steps with this library's kernels, each one design choice away from the
-rung before it; the side rows change one thing of the default kernel.
+rung before it, and R8 adds one of CDNA4's own (one wave per SIMD with a K
+loop free of scalar and vector arithmetic; the side row without that loop
+separates its two changes); the side rows change one thing of R7 or R8.
 
 Run (needs a GPU):
 
@@ -83,11 +85,15 @@ LADDER = [
      "five single-operand LDS slots: a step's loads spread over the whole step"),
     ("mfma16_256x256x64_w8_r5_l4_persistent", "R7",
      "persistent: one workgroup per CU walks its tiles, the next tile's loads start "
-     "under this tile's last steps, C staged through LDS (the default)"),
+     "under this tile's last steps, C staged through LDS"),
+    ("mfma16_256x256x64_w4_r5_persistent_lean", "R8",
+     "4 waves of 128x128, one per SIMD (accumulators in all 256 AGPRs, a third fewer LDS reads "
+     "per MFMA), with a K loop that holds no scalar or vector arithmetic: a cycle of five steps "
+     "with constant slot offsets, addresses kept in registers (the default)"),
 ]
 
-# (variant, what differs: from R1 for the first row, else from the default
-# kernel, R7)
+# (variant, what differs: from R1 for the first row, from R8 for the two
+# 4-wave rows, else from R7)
 SIDE = [
     ("mfma16_128x128x64_w4_s1",
      "R1 without the one-workgroup limit: its 32 KiB of LDS lets four workgroups share a CU, "
@@ -107,8 +113,8 @@ SIDE = [
     ("mfma16_256x256x64_w8_r5_l4_persistent_vacc",
      "accumulators in VGPRs instead of AGPRs (the epilogue converts them without moving them first)"),
     ("mfma16_256x256x64_w4_r5_persistent_rs2",
-     "4 waves of 128x128 (one per SIMD, accumulators in all 256 AGPRs): a third fewer LDS "
-     "reads per MFMA; fragment reads over the first half of each sub-step"),
+     "R8 without the lean K loop: every step computes its slot offsets, M0 values and load "
+     "addresses (a lone wave per SIMD pays for that arithmetic between its MFMAs)"),
     ("mfma16_256x256x64_w4_r5_persistent_rs2_m0",
      "the same, with each group of four global->LDS loads sharing one LDS base (M0)"),
     ("mfma16_256x256x64_w8_s2",

@@ -60,10 +60,10 @@ def test_selection(lib):
         assert 0 <= v < n
         assert binding.gemm_nt_f16_config_name(w.M, w.N, w.K).startswith("mfma")
     name = binding.gemm_nt_f16_config_name
-    assert name(8192, 8192, 8192) == "mfma16_256x256x64_w8_r5_l4_persistent"
-    assert name(4096, 4096, 4096) == "mfma16_256x256x64_w8_r5_l4_persistent"
-    assert name(5000, 3000, 6000) == "mfma16_256x256x64_w8_r5_l4_persistent"
-    assert name(4096, 4096, 1024) == "mfma16_256x256x64_w8_r5_l4_persistent"
+    assert name(8192, 8192, 8192) == "mfma16_256x256x64_w4_r5_persistent_lean"
+    assert name(4096, 4096, 4096) == "mfma16_256x256x64_w4_r5_persistent_lean"
+    assert name(5000, 3000, 6000) == "mfma16_256x256x64_w4_r5_persistent_lean"
+    assert name(4096, 4096, 1024) == "mfma16_256x256x64_w4_r5_persistent_lean"
     assert name(2048, 2048, 8192) == "mfma16_128x128x64_w8_s3_l4_ordered"
     assert name(2048, 2048, 2048) == "mfma16_128x128x64_w8_s3_l4_ordered"
     assert name(1024, 1024, 1024) == "mfma16_64x64x64_w4_s3"
@@ -165,7 +165,7 @@ def test_launch_plan_invariants_on_random_shapes(lib):
             assert rows == M, (M, N, K)
             continue
         splits += 1
-        assert names[v] == "mfma16_256x256x64_w8_r5_l4_persistent", (M, N, K)
+        assert names[v] == "mfma16_256x256x64_w4_r5_persistent_lean", (M, N, K)
         assert 0 < rows < M and rows % 256 == 0, (M, N, K, rows)
         assert 0 <= rest < len(names) and names[rest] != "simple_f32_per_element", (M, N, K)
         # w waves hold the first rows' tiles, and one more tile row would not fit
@@ -188,7 +188,7 @@ def test_launch_plan(lib):
     # a small last wave: whole waves over the first rows, the rest apart
     for shape in [(6144, 6144, 6144), (4352, 4352, 2048), (4104, 4096, 2048), (4200, 4352, 1024)]:
         v, rows, rest = plan(*shape)
-        assert names[v] == "mfma16_256x256x64_w8_r5_l4_persistent", shape
+        assert names[v] == "mfma16_256x256x64_w4_r5_persistent_lean", shape
         assert 0 < rows < shape[0] and rows % 256 == 0 and 0 <= rest < len(names), shape
         # the most whole tile rows that fit in w waves of 256 tiles
         tiles_n = (shape[1] + 255) // 256

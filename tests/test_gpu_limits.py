@@ -31,7 +31,7 @@ from dense_fp16_gemm_04_amd import binding
 pytestmark = pytest.mark.gpu
 
 SELECTABLE = [
-    "mfma16_256x256x64_w8_r5_l4_persistent",
+    "mfma16_256x256x64_w4_r5_persistent_lean",
     "mfma16_256x128x64_w8x_s3_l4_ordered",
     "mfma16_128x128x64_w8_s3_l4_ordered",
     "mfma16_64x64x64_w4_s3",
