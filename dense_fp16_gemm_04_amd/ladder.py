@@ -124,8 +124,15 @@ SIDE = [
 ]
 
 
-def rows():
-    return [(v, r, w) for v, r, w in LADDER] + [(v, "side", w) for v, w in SIDE]
+def rows(only=None):
+    """The rows in table order; with `only` (variant names), just those."""
+    r = [(v, r, w) for v, r, w in LADDER] + [(v, "side", w) for v, w in SIDE]
+    if only:
+        missing = set(only) - {v for v, _, _ in r}
+        if missing:
+            raise SystemExit("ladder: not a row: %s" % ", ".join(sorted(missing)))
+        r = [x for x in r if x[0] in set(only)]
+    return r
 
 
 def run(args) -> int:
@@ -146,7 +153,7 @@ def run(args) -> int:
     names = binding.variants()
     stream = torch.cuda.current_stream(dev)
     table = []
-    for name, rung, what in rows():
+    for name, rung, what in rows(args.only):
         vid = names.index(name)
 
         def step():
@@ -195,13 +202,13 @@ def _dispatches(d):
     return [disp[k] for k in sorted(disp)]
 
 
-def summarize(dirs, warmup, launches, times=None, workload="square_8192") -> int:
+def summarize(dirs, warmup, launches, times=None, workload="square_8192", only=None) -> int:
     from dense_fp16_gemm_04_amd import workloads
 
     w = workloads.by_name(workload)
-    order = rows()
+    order = rows(only)
     per = warmup + launches
-    table = {v: {} for v, _, _ in order}
+    runs = {v: [] for v, _, _ in order}  # per row: one {counter: median} per counter run
     for d in dirs:
         disp = _dispatches(d)
         if len(disp) != per * len(order):
@@ -210,30 +217,43 @@ def summarize(dirs, warmup, launches, times=None, workload="square_8192") -> int
             return 1
         for i, (v, _, _) in enumerate(order):
             chunk = disp[i * per + warmup:(i + 1) * per]
-            for c in chunk[0]:
-                table[v][c] = statistics.median(x[c] for x in chunk)
+            runs[v].append({c: statistics.median(x[c] for x in chunk) for c in chunk[0]})
+
+    def get(v, *names):
+        """The named counters of row v, all from the first run that counted
+        every one of them (a ratio never mixes two runs), else None."""
+        for r in runs[v]:
+            if all(n in r for n in names):
+                return [r[n] for n in names]
+        return None
+
     timed = {}
     if times:
         with open(times) as f:
             timed = {r["variant"]: r for r in json.loads(f.read().strip().splitlines()[-1])["rows"]}
     mfmas = w.flops / 16384  # 16x16x32 MFMAs the product needs
+
+    def ratio(v, f, *names):
+        x = get(v, *names)
+        try:
+            return None if x is None else f(*x)
+        except ZeroDivisionError:
+            return None
+
     fmt = lambda x, f: "-" if x is None else f % x
     print("| rung | variant | TFLOP/s | % of peak | MFMA busy | implied clock MHz | waves waiting | "
           "LDS instr / MFMA | SALU / MFMA | LDS bank conflicts | read beyond L2 GB | written GB | "
           "L2 hit | what changes |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for v, rung, what in order:
-        t = table[v]
-        cyc = t.get("GRBM_GUI_ACTIVE", 0) / 8
-        busy = 100 * t["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024) if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in t else None
-        wait = 100 * t["SQ_WAIT_ANY"] / t["SQ_WAVE_CYCLES"] if t.get("SQ_WAVE_CYCLES") else None
-        lds = t["SQ_INSTS_LDS"] / mfmas if "SQ_INSTS_LDS" in t else None
-        salu = t["SQ_INSTS_SALU"] / mfmas if "SQ_INSTS_SALU" in t else None
-        conf = 100 * t["SQ_LDS_BANK_CONFLICT"] / t["SQ_LDS_IDX_ACTIVE"] if t.get("SQ_LDS_IDX_ACTIVE") else None
-        rd = 32 * t["TCC_EA0_RDREQ_DRAM_32B_sum"] / 1e9 if "TCC_EA0_RDREQ_DRAM_32B_sum" in t else None
-        wr = (64 * t["TCC_EA0_WRREQ_64B_sum"] + 32 * (t["TCC_EA0_WRREQ_sum"] - t["TCC_EA0_WRREQ_64B_sum"])) / 1e9 \
-            if "TCC_EA0_WRREQ_sum" in t else None
-        hit = 100 * t["TCC_HIT_sum"] / t["TCC_REQ_sum"] if t.get("TCC_REQ_sum") and "TCC_HIT_sum" in t else None
+        busy = ratio(v, lambda m, g: 100 * m / (g / 8 * 1024), "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+        wait = ratio(v, lambda a, c: 100 * a / c, "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")
+        lds = ratio(v, lambda x: x / mfmas, "SQ_INSTS_LDS")
+        salu = ratio(v, lambda x: x / mfmas, "SQ_INSTS_SALU")
+        conf = ratio(v, lambda b, a: 100 * b / a, "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE")
+        rd = ratio(v, lambda x: 32 * x / 1e9, "TCC_EA0_RDREQ_DRAM_32B_sum")
+        wr = ratio(v, lambda a, b: (64 * b + 32 * (a - b)) / 1e9, "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")
+        hit = ratio(v, lambda h, r: 100 * h / r, "TCC_HIT_sum", "TCC_REQ_sum")
         tf = timed.get(v, {}).get("tflops")
         # the clock at which the timed rate and the counted busy fraction
         # agree: TFLOP/s = busy * 1024 SIMDs * 1024 flop/clock * clock
@@ -242,6 +262,26 @@ def summarize(dirs, warmup, launches, times=None, workload="square_8192") -> int
             rung, v, fmt(tf, "%.1f"), fmt(None if tf is None else 100 * tf / 2516.5824, "%.1f"),
             fmt(busy, "%.1f%%"), fmt(implied, "%.0f"), fmt(wait, "%.1f%%"), fmt(lds, "%.3f"), fmt(salu, "%.3f"),
             fmt(conf, "%.2f%%"), fmt(rd, "%.3f"), fmt(wr, "%.3f"), fmt(hit, "%.1f%%"), what))
+    # counters outside the main table, where a run collected them
+    extra = [("scalar-unit instr per cycle per CU", lambda a, g: a / (g / 8) / 256, "%.3f",
+              ("SQ_ACTIVE_INST_SCA", "GRBM_GUI_ACTIVE")),
+             ("vector instr per MFMA (MFMAs included)", lambda x: x / mfmas, "%.3f", ("SQ_INSTS_VALU",)),
+             ("waiting to issue an LDS instr", lambda a, c: 100 * a / c, "%.1f%%",
+              ("SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES")),
+             ("issue cycles per global->LDS load", lambda a, n: a / n, "%.2f",
+              ("SQ_INST_CYCLES_VMEM_RD", "SQ_INSTS_VMEM_RD")),
+             ("LDS busy", lambda a, g: 100 * a / (g / 8 * 256), "%.1f%%", ("SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")),
+             ("clock of the counted dispatches, MHz", lambda g, ns: g / 8 / (ns * 1e-9) / 1e6, "%.0f",
+              ("GRBM_GUI_ACTIVE", "ns"))]
+    present = [x for x in extra[:-1] if any(get(v, x[3][0]) is not None for v, _, _ in order)]
+    if present:
+        present.append(extra[-1])
+        print()
+        print("| variant | " + " | ".join(x[0] for x in present) + " |")
+        print("|---|" + "---|" * len(present))
+        for v, _, _ in order:
+            vals = [fmt(ratio(v, f, *names), form) for _, f, form, names in present]
+            print("| `%s` | %s |" % (v, " | ".join(vals)))
     return 0
 
 
@@ -253,9 +293,11 @@ def main(argv=None) -> int:
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--summarize", nargs="+", metavar="DIR", help="summarise rocprofv3 counter output")
     p.add_argument("--times", help="the JSON line of a timed run, for the TFLOP/s column")
+    p.add_argument("--only", type=lambda x: x.split(","), metavar="V1,V2,...",
+                   help="run (or summarise) only these rows, in table order")
     args = p.parse_args(argv)
     if args.summarize:
-        return summarize(args.summarize, args.warmup, args.launches, args.times, args.workload)
+        return summarize(args.summarize, args.warmup, args.launches, args.times, args.workload, args.only)
     return run(args)
 
 
