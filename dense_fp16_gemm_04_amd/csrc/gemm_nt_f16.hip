@@ -955,8 +955,9 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
 // registers (three copies 64 KiB apart, so that every offset fits the read's
 // 16-bit immediate), the loads keep their per-lane offsets in registers and
 // share M0 in groups of four, and the K position advances in one scalar
-// register.  Steps past the end of K and the two steps that start the next
-// tile keep the general form.
+// register.  Steps past the end of K, the two steps that start the next
+// tile, and up to four steps before a tile's first cycle and after its last
+// keep the general form (the ring position in a register).
 constexpr int kDirect = 1, kVgprAcc = 2, kColumns = 4, kSharedM0 = 8, kLean = 16;
 template <class T, int RS, int LS, int FLAGS = 0>
 __global__ void __launch_bounds__(T::THREADS, 1)
