@@ -165,22 +165,15 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
 //   STAGES    depth of the LDS ring: loads run STAGES - 1 steps ahead
 //   MIN_WAVES_PER_SIMD  occupancy hint (1: up to 512 registers per lane, the
 //             256 AGPRs holding the accumulator; 2: up to 256)
-//   EARLY     how many of a loading wave's global->LDS loads of a step are
-//             issued one step sooner, spread over the MFMAs before the
-//             barrier (needs STAGES >= 3); the others go out right after it
 //   LOADERS   how many waves issue the global->LDS loads (0: all of them);
 //             with half of the waves loading, each SIMD runs one wave that
 //             never waits on the vector memory queue and keeps the matrix
 //             core busy while its partner issues loads
-//   DIST      how many MFMA k sub-steps ahead the fragments are read from
-//             LDS (1 .. KK); with DIST = KK a whole step is read ahead, the
-//             barrier sits at the start of the step and the step's loads
-//             spread over all of its MFMAs
 //   MI        MFMA block: 32 (v_mfma_f32_32x32x16_f16) or 16
 //             (v_mfma_f32_16x16x32_f16: half the work per instruction, the
 //             same bytes of operands per flop from LDS)
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_, int EARLY_ = 0,
-          int LOADERS_ = 0, int DIST_ = 1, int MI_ = 32>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_, int LOADERS_ = 0,
+          int MI_ = 32>
 struct TileShape {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -213,10 +206,6 @@ struct TileShape {
     static constexpr int A_LOADS = A_BYTES / 1024 / LOADERS;       // 1 KiB per wave load
     static constexpr int B_LOADS = B_BYTES / 1024 / LOADERS;
     static constexpr int LOADS = A_LOADS + B_LOADS;                // per loading wave per step
-    static constexpr int EARLY = EARLY_, LATE = LOADS - EARLY_;
-    static constexpr int DIST = DIST_;
-    static constexpr int R1_MFMAS = (KK - DIST) * FM * FN;        // MFMAs before the barrier
-    static constexpr int R2_MFMAS = DIST * FM * FN;               // MFMAs after it
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(ROWS_PER_LINE * CHUNKS == 16, "swizzle covers 16 lanes");
     static_assert(MI == 32 || MI == 16, "MFMA block is 32x32 or 16x16");
@@ -226,14 +215,8 @@ struct TileShape {
     static_assert(B_LOADS * LOADERS * 1024 == B_BYTES, "B tile must split evenly over loading waves");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
     static_assert(STAGES >= 1 && LOADS * (STAGES - 2) <= 63, "vmcnt holds at most 63");
-    static_assert(STAGES >= 2 || (EARLY_ == 0 && DIST_ == 1), "a single stage is loaded, then computed");
-    static_assert(EARLY >= 0 && EARLY <= LOADS && (EARLY == 0 || STAGES >= 3),
-                  "early loads need a free stage one step ahead");
-    static_assert(DIST >= 1 && DIST <= KK, "fragments are read 1 .. KK sub-steps ahead");
-    static_assert(EARLY == 0 || DIST < KK, "early loads go before the barrier");
-    static_assert((DIST == KK || (EARLY + KK - DIST - 1) / (KK - DIST) <= 4 * FM * FN) &&
-                      (LATE + DIST - 1) / DIST <= 4 * FM * FN,
-                  "at most 4 loads per MFMA");
+    static_assert(KK % 2 == 0, "two fragment sets alternate by k sub-step");
+    static_assert(LOADS <= 4 * FM * FN, "at most 4 loads per MFMA");
 };
 
 // Scheduling group of n (0 .. 4, known after unrolling) vector memory
@@ -497,14 +480,9 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) fr_pos[kk] = swz<T>(fr_row, T::CPS * kk + fr_hi) * 16;
 
-    // Fragment registers.  With DIST = 1 and KK even two sets alternate by
-    // sub-step (sub-step kk always uses set kk % 2).  Otherwise set
-    // [p][kk] holds sub-step kk of a step with parity p; only the DIST + 1
-    // sets in flight are live at a time, and only those get registers.
-    constexpr bool ALT = T::DIST == 1 && T::KK % 2 == 0;  // sets alternate by sub-step
-    constexpr int NSETS = ALT ? 2 : 2 * T::KK;
-    half8_t fa[NSETS][T::FM], fb[NSETS][T::FN];
-    auto set_of = [](int p, int kk) { return ALT ? (kk & 1) : p * T::KK + kk; };
+    // Fragment registers: two sets alternate by k sub-step (sub-step kk
+    // uses set kk % 2; KK is even), each read one sub-step before its MFMAs.
+    half8_t fa[2][T::FM], fb[2][T::FN];
     typename T::acc_t acc[T::FM][T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
@@ -513,32 +491,30 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 #pragma unroll
             for (int r = 0; r < T::ACC; ++r) acc[i][j][r] = 0.0f;
 
-    auto read_frags = [&](int p, const unsigned char* stage_base, int kk) {
+    auto read_frags = [&](const unsigned char* stage_base, int kk) {
         const unsigned char* pa = stage_base + a_row0 * T::ROW_BYTES + fr_pos[kk];
         const unsigned char* pb = stage_base + T::A_BYTES + b_row0 * T::ROW_BYTES + fr_pos[kk];
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i) fa[set_of(p, kk)][i] = *(const half8_t*)(pa + i * T::MI * T::ROW_BYTES);
+        for (int i = 0; i < T::FM; ++i) fa[kk & 1][i] = *(const half8_t*)(pa + i * T::MI * T::ROW_BYTES);
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) fb[set_of(p, kk)][j] = *(const half8_t*)(pb + j * T::MI * T::ROW_BYTES);
+        for (int j = 0; j < T::FN; ++j) fb[kk & 1][j] = *(const half8_t*)(pb + j * T::MI * T::ROW_BYTES);
     };
 
     // When the accumulators fill all 256 AGPRs (one wave per SIMD, 16x16
     // blocks), MFMAs compiled from the builtin get their accumulators moved
     // between AGPRs and VGPRs inside the loop; asm MFMAs keep them in place.
     constexpr bool kAgprAcc = T::MI == 16 && T::OCC == 1 && T::FM * T::FN * T::ACC == 256;
-    auto mma = [&](int p, int kk) {
+    auto mma = [&](int kk) {
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
             for (int j = 0; j < T::FN; ++j)
                 if constexpr (T::MI == 32)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[set_of(p, kk)][j], fa[set_of(p, kk)][i],
-                                                                       acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
                 else if constexpr (kAgprAcc)
-                    mfma16_agpr(acc[i][j], fb[set_of(p, kk)][j], fa[set_of(p, kk)][i]);
+                    mfma16_agpr(acc[i][j], fb[kk & 1][j], fa[kk & 1][i]);
                 else
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[set_of(p, kk)][j], fa[set_of(p, kk)][i],
-                                                                       acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
     };
 
     const int nk = (K + T::BK - 1) / T::BK;
@@ -552,27 +528,17 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     // barrier), step ks's stage is free after it and is refilled with step
     // ks + STAGES.
     //
-    // Fragments of sub-step kk are read DIST sub-steps before its MFMAs, so
-    // a step splits at the barrier (pinned with scheduling-group barriers,
-    // so the matrix core always has independent work queued):
-    //   before:  sub-steps 0 .. KK-DIST-1: fragment reads of sub-step
-    //            kk+DIST, then the FM*FN MFMAs of sub-step kk;
-    //   after:   sub-steps KK-DIST .. KK-1: fragment reads of the next
-    //            step's sub-step kk+DIST-KK, then the MFMAs of sub-step kk,
-    //            with the step's loads spread between them.
-    //
-    // With EARLY > 0 a step's loads go out in two parts: the first LATE right
-    // after the barrier that frees their stage, the last EARLY during the
-    // next step's MFMAs before its barrier.  Spreading them keeps the vector
-    // memory queue short, so a load waiting for a queue slot does not hold up
-    // the MFMAs behind it.  Loads leave in the same order either way, so the
-    // vmcnt count at each barrier is unchanged: only the STAGES - 2 steps
-    // after the next one may be in flight.
+    // Fragments of sub-step kk are read one sub-step before its MFMAs, so a
+    // step splits at the barrier (pinned with scheduling-group barriers, so
+    // the matrix core always has independent work queued):
+    //   before:  sub-steps 0 .. KK-2: fragment reads of sub-step kk+1, then
+    //            the FM*FN MFMAs of sub-step kk;
+    //   after:   sub-step KK-1: fragment reads of the next step's sub-step
+    //            0, then its MFMAs, with the step's loads spread between them.
     //
     // The loop is compiled twice: for loading waves and, when only some
     // waves load, for the others (no loads, and nothing in flight at the
-    // barriers).  Unless the sets alternate by sub-step, its body covers two
-    // steps, so the fragment set parity is known at compile time.
+    // barriers).
     auto main_loop = [&](auto tag) {
         constexpr bool LD = decltype(tag)::value;
         if constexpr (T::STAGES == 1) {
@@ -586,86 +552,53 @@ gemm_nt_f16_mfma(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                 lds_barrier<0>();
 #pragma unroll
                 for (int kk = 0; kk < T::KK; ++kk) {
-                    read_frags(0, smem, kk);
-                    mma(0, kk);
+                    read_frags(smem, kk);
+                    mma(kk);
                 }
                 lds_barrier<0>();
             }
         } else {
-            if constexpr (T::EARLY == 0) {
-                // every stage is free at the start: fill them all, then wait
-                // for step 0 only
+            // every stage is free at the start: fill them all, then wait for
+            // step 0 only
 #pragma unroll
-                for (int s = 0; s < T::STAGES; ++s)
-                    if constexpr (LD) issue_loads(s, s);
-                lds_barrier<T::LOADS * (T::STAGES - 1)>();
-            } else {
-                // the early part of step STAGES - 1 goes out during step 0
-#pragma unroll
-                for (int s = 0; s < T::STAGES - 1; ++s)
-                    if constexpr (LD) issue_loads(s, s);
-                lds_barrier<T::LOADS * (T::STAGES - 2)>();
-                if constexpr (LD) issue_load_range(T::STAGES - 1, T::STAGES - 1, 0, T::LATE);
-            }
-#pragma unroll
-            for (int kk = 0; kk < T::DIST; ++kk) read_frags(0, smem, kk);
+            for (int s = 0; s < T::STAGES; ++s)
+                if constexpr (LD) issue_loads(s, s);
+            lds_barrier<T::LOADS * (T::STAGES - 1)>();
+            read_frags(smem, 0);
 
             int cur = 0;  // stage of step ks
-            auto step = [&](int ks, auto parity) {
-                constexpr int P = decltype(parity)::value;
+            auto step = [&](int ks) {
                 constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
                 const unsigned char* base = smem + cur * T::STAGE_BYTES;
                 const int nxt = cur + 1 == T::STAGES ? 0 : cur + 1;
-                const int prv = cur == 0 ? T::STAGES - 1 : cur - 1;  // free since the last barrier
                 // Each sub-step is its own scheduling region (fenced with
                 // sched_barrier), so MFMAs of different sub-steps never
                 // interleave into back-to-back dependent pairs.
 #pragma unroll
-                for (int kk = 0; kk < T::KK - T::DIST; ++kk) {
-                    constexpr int E = LD ? T::EARLY : 0;
-                    constexpr int R1 = T::KK - T::DIST > 0 ? T::KK - T::DIST : 1;
-                    const int e0 = E * kk / R1, e1 = E * (kk + 1) / R1;  // this sub-step's early loads
-                    read_frags(P, base, kk + T::DIST);
-                    mma(P, kk);
-                    if constexpr (E > 0) issue_load_range(prv, ks + T::STAGES - 1, T::LATE + e0, e1 - e0);
+                for (int kk = 0; kk < T::KK - 1; ++kk) {
+                    read_frags(base, kk + 1);
+                    mma(kk);
                     __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 0);  // DS reads
 #pragma unroll
-                    for (int i = 0; i < G; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-                        sched_vmem<0>((e1 - e0) * (i + 1) / G - (e1 - e0) * i / G);  // loads
-                    }
+                    for (int i = 0; i < G; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 lds_barrier<T::LOADS * (T::STAGES - 2)>();
                 __builtin_amdgcn_sched_barrier(0);
-                const unsigned char* next = smem + nxt * T::STAGE_BYTES;
+                constexpr int L = LD ? T::LOADS : 0;
+                read_frags(smem + nxt * T::STAGE_BYTES, 0);
+                mma(T::KK - 1);
+                if constexpr (L > 0) issue_load_range(cur, ks + T::STAGES, 0, L);
+                __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
 #pragma unroll
-                for (int d = 0; d < T::DIST; ++d) {
-                    constexpr int L = LD ? T::LATE : 0;
-                    const int l0 = L * d / T::DIST, l1 = L * (d + 1) / T::DIST;  // this sub-step's loads
-                    read_frags(1 - P, next, d);
-                    mma(P, T::KK - T::DIST + d);
-                    if constexpr (L > 0) issue_load_range(cur, ks + T::STAGES, l0, l1 - l0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, T::FM + T::FN, 1);  // DS reads
-#pragma unroll
-                    for (int i = 0; i < G; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);          // one MFMA
-                        sched_vmem<1>((l1 - l0) * (i + 1) / G - (l1 - l0) * i / G);  // loads
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < G; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // one MFMA
+                    sched_vmem<1>(L * (i + 1) / G - L * i / G);        // loads
                 }
+                __builtin_amdgcn_sched_barrier(0);
                 cur = nxt;
             };
-            if constexpr (ALT) {
-                for (int ks = 0; ks < nk; ++ks) step(ks, Int<0>{});
-            } else {
-                int ks = 0;
-                for (; ks + 1 < nk; ks += 2) {
-                    step(ks, Int<0>{});
-                    step(ks + 1, Int<1>{});
-                }
-                if (ks < nk) step(ks, Int<0>{});
-            }
+            for (int ks = 0; ks < nk; ++ks) step(ks);
         }
     };
     if (nk > 0) {
@@ -727,7 +660,7 @@ gemm_nt_f16_ordered(const _Float16* __restrict__ A, const _Float16* __restrict__
                     _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
                     int group_m, int c_vec)
 {
-    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && (T::WAVES == 4 || T::WAVES == 8),
+    static_assert(T::MI == 16 && T::KK == 2 && (T::WAVES == 4 || T::WAVES == 8),
                   "16x16x32 MFMAs, two sub-steps per step, one or two waves per SIMD");
     constexpr int S = T::STAGES;
     constexpr int G = T::FM * T::FN;  // MFMAs per sub-step
@@ -965,7 +898,7 @@ gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __re
                             _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
                             int group_m, int c_vec)
 {
-    static_assert(T::MI == 16 && T::KK == 2 && T::DIST == 1 && T::LOADERS == 4 &&
+    static_assert(T::MI == 16 && T::KK == 2 && T::LOADERS == 4 &&
                       (T::WAVES == 8 || T::WAVES == 4) && T::WAVES_M == 2 && T::NG == 1,
                   "16x16x32 MFMAs, two sub-steps per step, 2 x 4 waves of which 4 load, or 2 x 2 "
                   "waves that all load");
@@ -1479,26 +1412,13 @@ gemm_nt_f16_simple(const _Float16* __restrict__ A, const _Float16* __restrict__ 
 
 // ------------------------------------------------------------------ host --
 
-//                  BM   BN   BK  WM  WN  S  OCC EARLY LOADERS DIST
+//                  BM   BN   BK  WM  WN  S  OCC LOADERS MI
 typedef TileShape<256, 256, 64, 2, 4, 2, 2> T256_k64_s2_w8;
-typedef TileShape<256, 256, 64, 2, 2, 2, 1> T256_k64_s2_w4;
-typedef TileShape<256, 256, 32, 2, 4, 5, 2> T256_k32_s5_w8;
-typedef TileShape<256, 256, 32, 2, 4, 4, 2, 0, 0, 2> T256_k32_s4_w8_d2;
-typedef TileShape<256, 256, 64, 2, 4, 2, 2, 0, 4> T256_k64_s2_w8_l4;
-typedef TileShape<256, 256, 32, 2, 2, 5, 1, 4> T256_k32_s5_w4_e4;
-typedef TileShape<256, 256, 64, 2, 2, 2, 1, 0, 0, 1, 16> T256_k64_s2_w4_mi16;
-typedef TileShape<256, 256, 64, 2, 4, 2, 2, 0, 0, 1, 16> T256_k64_s2_w8_mi16;
-typedef TileShape<256, 256, 32, 2, 4, 4, 2, 0, 0, 1, 16> T256_k32_s4_w8_mi16;
-typedef TileShape<256, 256, 64, 4, 2, 2, 2, 0, 0, 1, 16> T256_k64_s2_w8x_mi16;
-typedef TileShape<256, 256, 64, 2, 4, 2, 2, 0, 4, 1, 16> T256_k64_s2_w8_l4_mi16;
-typedef TileShape<256, 128, 64, 2, 2, 3, 1, 0, 0, 1, 16> T256x128_k64_s3_w4_mi16;
-typedef TileShape<256, 128, 64, 2, 4, 3, 2, 0, 0, 1, 16> T256x128_k64_s3_w8_mi16;
-typedef TileShape<128, 128, 64, 2, 2, 3, 1, 0, 0, 1, 16> T128_k64_s3_w4_mi16;
-typedef TileShape<128, 128, 64, 2, 4, 3, 2, 0, 0, 1, 16> T128_k64_s3_w8_mi16;
-typedef TileShape<64, 64, 64, 2, 2, 3, 2, 0, 0, 1, 16> T64_k64_s3_w4_mi16;
-typedef TileShape<256, 128, 64, 2, 2, 3, 1> T256x128_k64_s3_w4;
-typedef TileShape<128, 128, 64, 2, 2, 3, 1> T128_k64_s3_w4;
-typedef TileShape<64, 64, 64, 2, 2, 3, 2> T64_k64_s3_w4;
+typedef TileShape<256, 256, 64, 2, 2, 2, 1, 0, 16> T256_k64_s2_w4_mi16;
+typedef TileShape<256, 256, 64, 2, 4, 2, 2, 0, 16> T256_k64_s2_w8_mi16;
+typedef TileShape<256, 256, 64, 2, 4, 2, 2, 4, 16> T256_k64_s2_w8_l4_mi16;
+typedef TileShape<128, 128, 64, 2, 2, 3, 1, 0, 16> T128_k64_s3_w4_mi16;
+typedef TileShape<64, 64, 64, 2, 2, 3, 2, 0, 16> T64_k64_s3_w4_mi16;
 
 constexpr int64_t kMaxK = (int64_t)1 << 22;
 constexpr int64_t kMaxMN = ((int64_t)1 << 31) - 1;
@@ -1611,22 +1531,11 @@ int launch_simple(const void* A, const void* B, void* C, int64_t M, int64_t N, i
 }
 
 // The variants select_mfma chooses from (kCandidates) are the defaults; the
-// others are kept as the measured alternatives (tile shape, ring depth,
-// persistence, hand-scheduled issue order).
+// others are the rungs and side rows of the ablation ladder (tile shape,
+// ring depth, persistence, hand-scheduled issue order, one wave per SIMD).
 constexpr Variant kVariants[] = {
     {"mfma32_256x256x64_w8_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8>},
-    {"mfma32_256x256x64_w4_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w4>},
-    {"mfma32_256x256x32_w8_s5", 256, 256, 8, launch_mfma<T256_k32_s5_w8>},
-    {"mfma32_256x256x32_w8_s4_d2", 256, 256, 8, launch_mfma<T256_k32_s4_w8_d2>},
-    {"mfma32_256x256x64_w8_s2_l4", 256, 256, 8, launch_mfma<T256_k64_s2_w8_l4>},
-    {"mfma32_256x256x32_w4_s5_e4", 256, 256, 8, launch_mfma<T256_k32_s5_w4_e4>},
-    {"mfma16_256x256x64_w4_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w4_mi16>},
     {"mfma16_256x256x64_w8_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8_mi16>},
-    {"mfma16_256x256x32_w8_s4", 256, 256, 8, launch_mfma<T256_k32_s4_w8_mi16>},
-    {"mfma16_256x256x64_w8x_s2", 256, 256, 8, launch_mfma<T256_k64_s2_w8x_mi16>},
-    {"mfma16_256x256x64_w8_s2_l4", 256, 256, 8, launch_mfma<T256_k64_s2_w8_l4_mi16>},
-    {"mfma16_256x256x64_w4_s2_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w4_mi16, 4, 4>},
-    {"mfma16_256x128x64_w4_s3_ordered", 256, 128, 8, launch_ordered<T256x128_k64_s3_w4_mi16, 2, 2>},
     {"mfma16_256x256x64_w8_s2_l4_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w8_l4_mi16, 2, 2>},
     {"mfma16_256x256x64_w8_r5_l4_ordered", 256, 256, 8, launch_ordered<T256_k64_s2_w8_l4_mi16, 2, 2, true>},
     {"mfma16_256x256x64_w8_r5_l4_persistent", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2>},
@@ -1641,23 +1550,15 @@ constexpr Variant kVariants[] = {
      launch_ordered_persist<T256_k64_s2_w8_l4_mi16, 2, 2, kColumns>},
     {"mfma16_256x256x64_w4_r5_persistent_rs2_m0", 256, 256, 8,
      launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8, kSharedM0>},
-    {"mfma16_256x256x64_w4_r5_persistent", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 4, 8>},
     {"mfma16_256x256x64_w4_r5_persistent_rs2", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 2, 8>},
     {"mfma16_256x256x64_w4_r5_persistent_lean", 256, 256, 8, launch_ordered_persist<T256_k64_s2_w4_mi16, 3, 8, kLean>},
-    {"mfma16_256x128x64_w8_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
-    {"mfma16_256x128x64_w8x_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 4, 2, 3, 2, 0, 4, 1, 16>, 1, 1>},
-    {"mfma16_128x128x64_w8_s3_l4_ordered", 128, 128, 8, launch_ordered<TileShape<128, 128, 64, 2, 4, 3, 2, 0, 4, 1, 16>, 1, 1>},
-    {"mfma16_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4_mi16>},
-    {"mfma16_256x128x64_w8_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w8_mi16>},
-    {"mfma16_128x128x64_w4_s1", 128, 128, 8, launch_mfma<TileShape<128, 128, 64, 2, 2, 1, 2, 0, 0, 1, 16>>},
+    {"mfma16_256x128x64_w8x_s3_l4_ordered", 256, 128, 8, launch_ordered<TileShape<256, 128, 64, 4, 2, 3, 2, 4, 16>, 1, 1>},
+    {"mfma16_128x128x64_w8_s3_l4_ordered", 128, 128, 8, launch_ordered<TileShape<128, 128, 64, 2, 4, 3, 2, 4, 16>, 1, 1>},
+    {"mfma16_128x128x64_w4_s1", 128, 128, 8, launch_mfma<TileShape<128, 128, 64, 2, 2, 1, 2, 0, 16>>},
     {"mfma16_128x128x64_w4_s1_one_per_cu", 128, 128, 8,
-     launch_mfma_one_per_cu<TileShape<128, 128, 64, 2, 2, 1, 2, 0, 0, 1, 16>>},
+     launch_mfma_one_per_cu<TileShape<128, 128, 64, 2, 2, 1, 2, 0, 16>>},
     {"mfma16_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4_mi16>},
-    {"mfma16_128x128x64_w8_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w8_mi16>},
     {"mfma16_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4_mi16>},
-    {"mfma32_256x128x64_w4_s3", 256, 128, 8, launch_mfma<T256x128_k64_s3_w4>},
-    {"mfma32_128x128x64_w4_s3", 128, 128, 8, launch_mfma<T128_k64_s3_w4>},
-    {"mfma32_64x64x64_w4_s3", 64, 64, 8, launch_mfma<T64_k64_s3_w4>},
     {"simple_f32_per_element", 0, 0, 0, launch_simple},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
