@@ -29,8 +29,6 @@ from __future__ import annotations
 import argparse
 import json
 import os
-import shutil
-import statistics
 import subprocess
 import sys
 import time
@@ -143,122 +141,17 @@ def under_profiler() -> bool:
     return any(k.startswith("ROCPROF") for k in os.environ)
 
 
-def smi_command(*args):
-    """amd-smi's command line, its Python entry script run directly by this
-    interpreter; None when amd-smi is not installed."""
-    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
-    if not os.path.exists(exe):
-        return None
-    real = os.path.realpath(exe)
-    return ([sys.executable, real] if real.endswith(".py") else [real]) + list(args)
-
-
-def smi_json(*args):
-    cmd = smi_command(*args, "--json")
-    if cmd is None:
-        return None
-    try:
-        res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True, timeout=30)
-        out = res.stdout
-        return json.loads(out[min(i for i in (out.find("{"), out.find("[")) if i >= 0):])
-    except (OSError, ValueError, subprocess.SubprocessError):
-        return None
-
-
-def smi_sampler() -> int:
-    """The --smi-sampler child: started before the parent touches the GPU, it
-    waits for a line on stdin, then queries amd-smi for every GPU's engine
-    clocks and socket power until a second line (or end of input) arrives,
-    and prints {"bdf": {gpu: PCI address}, "samples": [[gpu, MHz, W], ...]}."""
-    import select
-
-    fd = sys.stdin.fileno()  # raw reads: no buffered line may hide the second one
-    if not os.read(fd, 64):
-        return 0
-    bdf = {}
-    for g in smi_json("list") or []:
-        if isinstance(g, dict) and "gpu" in g:
-            bdf[str(g["gpu"])] = str(g.get("bdf", "")).lower()
-    samples = []
-    while True:
-        d = smi_json("metric", "-c", "-p")
-        for g in (d or {}).get("gpu_data", []) if isinstance(d, dict) else []:
-            try:
-                clks = [v["clk"]["value"] for k, v in g["clock"].items()
-                        if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
-                samples.append([str(g["gpu"]), sum(clks) / len(clks), float(g["power"]["socket_power"]["value"])])
-            except (KeyError, TypeError, ValueError, ZeroDivisionError, AttributeError):
-                pass
-        if select.select([fd], [], [], 0)[0] or d is None:
-            break
-    print(json.dumps({"bdf": bdf, "samples": samples}), flush=True)
-    return 0
-
-
-def samples_of(got, domain, bus):
-    """The (MHz, W) samples of the GPU at PCI domain:bus in the sampler's
-    output; all of them when amd-smi lists a single GPU."""
-    want = "%04x:%02x:" % (domain, bus)
-    ids = [k for k, v in got.get("bdf", {}).items() if v.startswith(want)]
-    if not ids and len(got.get("bdf", {})) == 1:
-        ids = list(got["bdf"])
-    return [(c, w) for g, c, w in got.get("samples", []) if ids and g == ids[0]]
-
-
-def tell(sampler, line):
-    """One line to the sampler; it may already have ended (amd-smi failing)."""
-    try:
-        sampler.stdin.write(line + "\n")
-        sampler.stdin.flush()
-    except OSError:
-        pass
+# the amd-smi sampler child and the clock window live in the package (the
+# power-ceiling probe uses them too); bench.py --smi-sampler runs the child
+from dense_fp16_gemm_04_amd import clock as _clock  # noqa: E402
+from dense_fp16_gemm_04_amd.clock import samples_of, smi_command, smi_sampler, tell  # noqa: E402,F401
 
 
 def clock_window(sampler, seconds, step, stream, flops, props):
     """Back-to-back launches for `seconds` while the sampler child polls
     amd-smi: the engine clock and board power under sustained load, and the
     fraction of the peak at that clock."""
-    import torch
-
-    s0 = torch.cuda.Event(enable_timing=True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    for _ in range(5):  # reach load before the first sample
-        step()
-    torch.cuda.synchronize()
-    s0.record(stream)
-    tell(sampler, "start")
-    n, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(20):
-            step()
-        n += 20
-        torch.cuda.synchronize()
-    e0.record(stream)
-    tell(sampler, "stop")
-    torch.cuda.synchronize()
-    try:
-        got = json.loads(sampler.communicate(timeout=60)[0].strip().splitlines()[-1])
-    except (ValueError, IndexError, subprocess.SubprocessError):
-        log("bench: amd-smi gave no samples; no clock window")
-        return None
-    mine = samples_of(got, props.pci_domain_id, props.pci_bus_id)
-    if not mine:
-        log("bench: amd-smi gave no samples for this GPU; no clock window")
-        return None
-    ms = s0.elapsed_time(e0) / n
-    tflops = flops / (ms * 1e-3) / 1e12
-    clk = [c for c, _ in mine]
-    pw = [w for _, w in mine]
-    # the median: the first sample may still see the clock of the ramp-up
-    mhz = statistics.median(clk)
-    rec = {"seconds": seconds, "launches": n, "ms_per_launch": ms, "tflops": tflops,
-           "samples": len(mine), "sclk_mhz_median": mhz, "sclk_mhz_mean": statistics.mean(clk),
-           "sclk_mhz_range": [min(clk), max(clk)], "power_w_mean": statistics.mean(pw), "power_w_max": max(pw),
-           "pct_of_peak_at_sclk": 100 * tflops / (PEAK_TFLOPS * mhz / 2400.0),
-           "source": "amd-smi metric -c -p (engine clock averaged over the XCDs)"}
-    log("bench: %.1f s of launches: %.1f TFLOP/s at %.0f MHz median engine clock, %.0f W; %.1f%% of the peak "
-        "at that clock" % (seconds, tflops, mhz, rec["power_w_mean"], rec["pct_of_peak_at_sclk"]))
-    return rec
+    return _clock.clock_window(sampler, seconds, step, stream, flops, props, PEAK_TFLOPS)
 
 
 def main(argv=None) -> int:

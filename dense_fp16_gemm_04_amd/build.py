@@ -1,7 +1,8 @@
-"""Build the gfx950 library ``libgemm_nt_f16.so`` in this package directory.
+"""Build the gfx950 libraries in this package directory: ``libgemm_nt_f16.so``
+(the GEMM kernels and their C ABI) and ``libpower_probe.so`` (the power
+probe, a measuring instrument that the GEMM path never loads).
 
-One hipcc invocation compiles the HIP kernels and the C ABI ahead of time for
-gfx950 only.  ``-Xclang -target-feature -Xclang -packed-fp32-ops`` keeps the
+One hipcc invocation per library compiles it ahead of time for gfx950 only.  ``-Xclang -target-feature -Xclang -packed-fp32-ops`` keeps the
 compiler from emitting packed fp32 arithmetic (v_pk_*_f32); the host pass
 warns that it does not know the feature, which is harmless.
 
@@ -10,8 +11,8 @@ The same invocation asks the compiler for each kernel's resource usage
 occupancy, LDS).  The build fails if any kernel in the library uses scratch
 memory or spills registers: a spill puts per-lane scratch traffic into the
 K loop and slows a kernel by tens of percent without changing its results,
-so nothing else would notice.  The table is written beside the library as
-``libgemm_nt_f16.resources.json``.
+so nothing else would notice.  The table is written beside each library as
+``<library>.resources.json``.
 """
 from __future__ import annotations
 
@@ -28,6 +29,9 @@ SRC = os.path.join(HERE, "csrc", "gemm_nt_f16.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgemm_nt_f16.so")
 RESOURCES = os.path.join(HERE, "libgemm_nt_f16.resources.json")
+PROBE_SRC = os.path.join(HERE, "csrc", "power_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libpower_probe.so")
+PROBE_RESOURCES = os.path.join(HERE, "libpower_probe.resources.json")
 ARCH = "gfx950"
 
 
@@ -87,9 +91,9 @@ def spilling(kernels: dict) -> list:
                   if r.get("scratch_bytes_per_lane", 0) or r.get("vgpr_spill", 0) or r.get("sgpr_spill", 0))
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *flags(), "-Rpass-analysis=kernel-resource-usage", *extra, SRC, "-o", tmp]
+def compile_library(src: str, lib: str, resources: str, verbose: bool = False, extra=()) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *flags(), "-Rpass-analysis=kernel-resource-usage", *extra, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -109,10 +113,18 @@ def build(verbose: bool = False, extra=()) -> str:
                            "\n".join("  %s: %s" % (k, kernels[k]) for k in bad))
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    with open(RESOURCES + ".tmp", "w") as f:
+    with open(resources + ".tmp", "w") as f:
         json.dump({"arch": ARCH, "kernels": kernels}, f, indent=1, sort_keys=True)
-    os.replace(RESOURCES + ".tmp", RESOURCES)
-    os.replace(tmp, LIB)
+    os.replace(resources + ".tmp", resources)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Both libraries (`extra` flags for the GEMM library only); returns the
+    GEMM library's path."""
+    compile_library(SRC, LIB, RESOURCES, verbose, extra)
+    compile_library(PROBE_SRC, PROBE_LIB, PROBE_RESOURCES, verbose)
     return LIB
 
 

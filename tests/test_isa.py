@@ -11,18 +11,9 @@ the library built here.
 """
 from __future__ import annotations
 
-import collections
-import os
-import re
-import shutil
-import subprocess
-
-import pytest
-
+import _isa
 from dense_fp16_gemm_04_amd import binding
 
-LLVM = "/opt/rocm/llvm/bin"
-TOOLS = ("llvm-objcopy", "clang-offload-bundler", "llvm-objdump")
 # gemm_nt_f16_ordered_persist<TileShape<256,256,64,2,2,2,1,0,16>, RS=3, LS=8, kLean>
 LEAN_SYMBOL = ("gemm_nt_f16_ordered_persist", "ILi256ELi256ELi64ELi2ELi2ELi2ELi1ELi0ELi16EEELi3ELi8ELi16EEE")
 
@@ -33,52 +24,11 @@ READS_PER_CYCLE = 5 * 2 * (8 + 8)  # one b128 fragment per 16-row tile and K hal
 LOADS_PER_CYCLE = 5 * (8 + 8)      # A and B: 8 x 16 bytes per lane each
 
 
-def _disassemble(tmp_path) -> str:
-    lib = binding.library_path()
-    if not os.path.exists(lib):
-        pytest.skip("library not built")
-    for t in TOOLS:
-        if not os.path.exists(os.path.join(LLVM, t)):
-            pytest.skip("%s not installed" % t)
-    fatbin = str(tmp_path / "fatbin.bin")
-    co = str(tmp_path / "gfx950.o")
-    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section=.hip_fatbin=" + fatbin, lib, str(tmp_path / "x.so")],
-                   check=True, capture_output=True)
-    subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle", "--type=o", "--input=" + fatbin,
-                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", "--output=" + co], check=True, capture_output=True)
-    out = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", co],
-                         check=True, capture_output=True, text=True)
-    return out.stdout
-
-
-def _kernel(asm: str, parts) -> list:
-    """(address, mnemonic, branch target address or None) of one kernel."""
-    lines = asm.splitlines()
-    starts = [i for i, l in enumerate(lines) if l.endswith(">:") and all(p in l for p in parts)]
-    assert len(starts) == 1, "expected one kernel matching %s, found %d" % (parts, len(starts))
-    ins = []
-    for l in lines[starts[0] + 1:]:
-        if not l.strip():
-            break
-        m = re.match(r"\s+(\S+).*?//\s*([0-9A-F]+):", l)
-        if not m:
-            continue
-        t = re.search(r"\+0x([0-9a-f]+)>\s*$", l) if "branch" in m.group(1) else None
-        ins.append((int(m.group(2), 16), m.group(1), int(t.group(1), 16) if t else None))
-    base = ins[0][0]
-    return [(a, mn, None if t is None else base + t) for a, mn, t in ins]
-
-
 def test_lean_k_loop_holds_only_mfma_lds_loads_and_a_few_scalar_adds(tmp_path):
-    ins = _kernel(_disassemble(tmp_path), LEAN_SYMBOL)
-    loops = []
-    for a, mn, t in ins:
-        if t is not None and t <= a:  # a backward branch closes a loop
-            body = collections.Counter(m for x, m, _ in ins if t <= x <= a)
-            if sum(v for k, v in body.items() if k.startswith("v_mfma")) == MFMA_PER_CYCLE:
-                loops.append(body)
-    assert loops, "no loop of %d MFMAs in the lean kernel" % MFMA_PER_CYCLE
-    for body in loops:
+    ins = _isa.kernel(_isa.disassemble(binding.library_path(), tmp_path), LEAN_SYMBOL)
+    found = _isa.loops(ins, MFMA_PER_CYCLE)
+    assert found, "no loop of %d MFMAs in the lean kernel" % MFMA_PER_CYCLE
+    for body in found:
         assert body["v_mfma_f32_16x16x32_f16"] == MFMA_PER_CYCLE, body
         # no vector arithmetic at all: every v_ instruction is an MFMA
         vector = {k: v for k, v in body.items() if k.startswith("v_") and not k.startswith("v_mfma")}
