@@ -21,6 +21,9 @@
 //           stays resident in every L2, into LDS bytes [64 KiB, 128 KiB);
 //   kBarrier: once per step, between its two sub-steps, the wait for all but
 //           the last 8 loads and the LDS reads, then s_barrier;
+//   kVgprLoads: the other set's 8 B fragments of each sub-step loaded from
+//           the same L2-resident window straight into VGPRs (16-byte buffer
+//           loads, the same bytes per step as kLoads), no LDS;
 //   kZero: fragments of zeros instead of the Gaussian data;
 //   kMfma32: MFMAs alone as v_mfma_f32_32x32x16_f16 on 4 x 4 blocks of
 //           32 x 32 (the same 256 accumulators, the same 128 fragment
@@ -37,9 +40,9 @@
 // the loop and [65536, 131072) by the loads (64 KiB + 16 KiB * wave + 1 KiB
 // * load); global reads within src_bytes (a power of two, 64 MiB to 1 GiB:
 // the start-up reads are masked to it, and a load's offset, at most 4 KiB *
-// 3 + 1008 + 256 KiB * 3 + 64 KiB * 3 + 3 KiB, plus 16 bytes, stays below
-// 1 MiB); global
-// writes: one float per thread of sink[grid * 256].
+// 3 + 1008 + 256 KiB * 3 + 64 KiB * 3 + 3 KiB (kLoads) or 4 KiB * 3 + 1008 +
+// 256 KiB * 3 + 16 KiB * 15 (kVgprLoads), plus 16 bytes, stays below 1 MiB);
+// global writes: one float per thread of sink[grid * 256].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,7 +52,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kReads = 1, kLoads = 2, kBarrier = 4, kZero = 8, kMfma32 = 16;
+constexpr int kReads = 1, kLoads = 2, kBarrier = 4, kZero = 8, kMfma32 = 16, kVgprLoads = 32;
 // buffer resource word 3 for gfx950 raw buffer accesses (32-bit data format)
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -110,7 +113,9 @@ template <int MODE>
 __global__ void __launch_bounds__(256, 1)
 power_probe_kernel(const _Float16* __restrict__ src, uint32_t src_bytes, float* __restrict__ sink, int steps)
 {
-    constexpr bool RD = MODE & kReads, LD = MODE & kLoads, BAR = MODE & kBarrier, ZERO = MODE & kZero;
+    constexpr bool RD = MODE & kReads, LD = MODE & kLoads, BAR = MODE & kBarrier, ZERO = MODE & kZero,
+                   VL = MODE & kVgprLoads;
+    static_assert(!(VL && (RD || LD)), "register loads replace the LDS path");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[160 * 1024];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -168,6 +173,13 @@ power_probe_kernel(const _Float16* __restrict__ src, uint32_t src_bytes, float* 
                             fa[1 - cs][15 - idx] = *(const half8_t*)p;
                     }
                 }
+                if constexpr (VL) {
+                    if (t % 8 == 4) {
+                        const int l = cs * 8 + t / 8;
+                        fb[1 - cs][t / 8] = __builtin_bit_cast(
+                            half8_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, soff + (uint32_t)l * 16384u, 0));
+                    }
+                }
                 if constexpr (LD) {
                     if (t % 8 == 4) {
                         // load l = 4 * grp + r: LDS base (M0) and global offset
@@ -209,6 +221,7 @@ const Mode kModes[] = {
     {"mfma_lds_reads_loads", kReads | kLoads, power_probe_kernel<kReads | kLoads>},
     {"k_loop_mix", kReads | kLoads | kBarrier, power_probe_kernel<kReads | kLoads | kBarrier>},
     {"mfma32", kMfma32, power_probe_mfma32},
+    {"mfma_vgpr_loads", kVgprLoads, power_probe_kernel<kVgprLoads>},
 };
 constexpr int kNumModes = sizeof(kModes) / sizeof(kModes[0]);
 

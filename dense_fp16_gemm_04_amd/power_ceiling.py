@@ -49,6 +49,7 @@ ROWS = [
     ("mfma_lds_reads_loads", "MFMAs + the reads + the loads"),
     ("k_loop_mix", "MFMAs + reads + loads + one barrier per 128 MFMAs: the default kernel's K-loop mix"),
     ("mfma32", "MFMAs only as 32x32x16 (64 per step, the same flops), Gaussian fragments"),
+    ("mfma_vgpr_loads", "MFMAs + the same 16 loads per 128 MFMAs into VGPRs (the B fragments), no LDS"),
 ]
 
 

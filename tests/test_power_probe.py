@@ -70,6 +70,8 @@ def test_full_mix_issues_what_the_default_k_loop_issues(tmp_path):
         body = _probe_loop(probe, flags)
         assert body["ds_read_b128"] == reads and body["buffer_load_dwordx4"] == loads, (flags, body)
         assert body["s_barrier"] == 0, (flags, body)
+    direct = _probe_loop(probe, 32)
+    assert direct["buffer_load_dwordx4"] == 16 and direct["ds_read_b128"] == 0 and direct["s_barrier"] == 0, direct
     wide = _isa.loops(_isa.kernel(probe, ("power_probe_mfma32",)), 64)
     assert len(wide) == 1 and wide[0]["v_mfma_f32_32x32x16_f16"] == 64, wide
     assert not [k for k in wide[0] if k.startswith(("v_", "ds_", "buffer_")) and not k.startswith("v_mfma")], wide
