@@ -1,6 +1,7 @@
 """Host logic of bench.py (no GPU): the one-GPU guard, argument checks and
 the fresh-process repeat that reports the median run, and the amd-smi clock
-sampler (run against a stand-in amd-smi script)."""
+sampler (run against a stand-in amd-smi script), both as bench.py starts it
+and as the package's clock module does."""
 from __future__ import annotations
 
 import json
@@ -8,7 +9,10 @@ import subprocess
 import sys
 import types
 
+import pytest
+
 import bench
+from dense_fp16_gemm_04_amd import clock
 
 
 def test_more_than_one_gpu_is_refused(capsys):
@@ -59,7 +63,13 @@ else:
 '''
 
 
-def test_clock_sampler_protocol(tmp_path):
+# the sampler child as bench.py starts it, and as clock.start_sampler() does
+SAMPLER_COMMANDS = {"bench": [sys.executable, bench.__file__, "--smi-sampler"],
+                    "clock": [sys.executable, clock.__file__]}
+
+
+@pytest.mark.parametrize("entry", sorted(SAMPLER_COMMANDS))
+def test_clock_sampler_protocol(tmp_path, entry):
     """The sampler waits for a first line, queries until a second one, and
     reports every GPU's mean engine clock over the XCDs and its power;
     samples_of picks the GPU by PCI address."""
@@ -68,7 +78,7 @@ def test_clock_sampler_protocol(tmp_path):
     script.chmod(0o755)
     (tmp_path / "amd-smi").symlink_to(script)
     env = dict(__import__("os").environ, PATH="%s:%s" % (tmp_path, __import__("os").environ.get("PATH", "")))
-    proc = subprocess.Popen([sys.executable, bench.__file__, "--smi-sampler"], stdin=subprocess.PIPE,
+    proc = subprocess.Popen(SAMPLER_COMMANDS[entry], stdin=subprocess.PIPE,
                             stdout=subprocess.PIPE, text=True, env=env)
     proc.stdin.write("start\n")
     proc.stdin.flush()
@@ -86,9 +96,9 @@ def test_clock_sampler_protocol(tmp_path):
     assert bench.samples_of(got, 0, 0x99) == []
 
 
-def test_clock_sampler_without_a_start_line_exits():
-    proc = subprocess.run([sys.executable, bench.__file__, "--smi-sampler"], input="", stdout=subprocess.PIPE,
-                          text=True, timeout=60)
+@pytest.mark.parametrize("entry", sorted(SAMPLER_COMMANDS))
+def test_clock_sampler_without_a_start_line_exits(entry):
+    proc = subprocess.run(SAMPLER_COMMANDS[entry], input="", stdout=subprocess.PIPE, text=True, timeout=60)
     assert proc.returncode == 0 and proc.stdout == ""
 
 
