@@ -896,7 +896,7 @@ template <class T, int RS, int LS, int FLAGS = 0>
 __global__ void __launch_bounds__(T::THREADS, 1)
 gemm_nt_f16_ordered_persist(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                             _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
-                            int group_m, int c_vec)
+                            int group_m)
 {
     static_assert(T::MI == 16 && T::KK == 2 && T::LOADERS == 4 &&
                       (T::WAVES == 8 || T::WAVES == 4) && T::WAVES_M == 2 && T::NG == 1,
@@ -1500,7 +1500,7 @@ int launch_ordered_persist(const void* A, const void* B, void* C, int64_t M, int
         return launch_ordered<T, RS, LS, true>(A, B, C, M, N, K, group_m, stream);
     hipLaunchKernelGGL((gemm_nt_f16_ordered_persist<T, RS, LS, FLAGS>), dim3((unsigned)grid), dim3(T::THREADS), 0,
                        stream, (const _Float16*)A, (const _Float16*)B, (_Float16*)C, (int)M, (int)N, (int)K,
-                       (int)tiles_m, (int)tiles_n, group_m, c_vec);
+                       (int)tiles_m, (int)tiles_n, group_m);
     return (int)hipGetLastError();
 }
 
