@@ -43,6 +43,21 @@ def test_launch_rejects_arguments_outside_its_ranges(lib):
         assert rc == HIP_ERROR_INVALID_VALUE, bad
 
 
+def test_probe_kernels_do_not_spill(lib):
+    """The build gate covers the probe library too: every mode's kernel is
+    in its resource record, none with scratch, one wave per SIMD."""
+    import json
+
+    from dense_fp16_gemm_04_amd import build
+
+    with open(build.PROBE_RESOURCES) as f:
+        kernels = json.load(f)["kernels"]
+    assert len(kernels) == len(power_ceiling.ROWS)
+    assert build.spilling(kernels) == []
+    for name, r in kernels.items():
+        assert r["agprs"] == 256 and r["waves_per_simd"] == 1, (name, r)
+
+
 def _probe_loop(asm, flags):
     found = _isa.loops(_isa.kernel(asm, ("power_probe_kernelILi%dE" % flags,)), 128)
     assert len(found) == 1, (flags, found)
