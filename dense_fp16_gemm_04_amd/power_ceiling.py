@@ -154,9 +154,9 @@ def main(argv=None) -> int:
             for _ in range(10):
                 step()
             torch.cuda.synchronize()
-        print("power_ceiling: %s" % label, file=sys.stderr, flush=True)
         if sampler is not None:
-            rec = clock.clock_window(sampler, args.window, step, stream, flops, props, PEAK_TFLOPS, label="  ")
+            rec = clock.clock_window(sampler, args.window, step, stream, flops, props, PEAK_TFLOPS,
+                                     label="power_ceiling: " + label)
             if rec is not None:
                 return rec
         return timed_only(args.window, step, stream, flops)
