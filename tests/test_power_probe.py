@@ -107,6 +107,12 @@ def test_table_reads_against_mfma_only():
     assert t[5].endswith("| - | - | - | - | - | - |")
 
 
+def test_driver_rejects_bad_arguments_before_starting_anything(capsys):
+    for bad in (["--steps", "0"], ["--window", "0"], ["--settle", "-1"]):
+        assert power_ceiling.main(bad) == 2, bad
+    assert "power_ceiling:" in capsys.readouterr().err
+
+
 @pytest.mark.gpu
 def test_every_mode_launches_and_finishes(lib):
     import torch
