@@ -49,33 +49,45 @@ def smi_json(*args):
 
 
 def smi_sampler() -> int:
-    """The sampler child: waits for a line on stdin, then queries amd-smi for
-    every GPU's engine clocks and socket power until a second line (or end of
-    input) arrives, and prints {"bdf": {gpu: PCI address}, "samples": [[gpu,
-    MHz, W], ...]}."""
+    """The sampler child, one window after another: it waits for a line on
+    stdin, then queries amd-smi for every GPU's engine clocks and socket power
+    until the next line (or end of input) arrives, and prints one line
+    {"bdf": {gpu: PCI address}, "samples": [[gpu, MHz, W], ...]}.  It exits
+    at end of input, or when amd-smi fails."""
     import select
 
-    fd = sys.stdin.fileno()  # raw reads: no buffered line may hide the second one
-    if not os.read(fd, 64):
-        return 0
-    bdf = {}
-    for g in smi_json("list") or []:
-        if isinstance(g, dict) and "gpu" in g:
-            bdf[str(g["gpu"])] = str(g.get("bdf", "")).lower()
-    samples = []
+    fd = sys.stdin.fileno()  # raw reads: no buffered line may hide the next one
+    bdf = None
     while True:
-        d = smi_json("metric", "-c", "-p")
-        for g in (d or {}).get("gpu_data", []) if isinstance(d, dict) else []:
-            try:
-                clks = [v["clk"]["value"] for k, v in g["clock"].items()
-                        if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
-                samples.append([str(g["gpu"]), sum(clks) / len(clks), float(g["power"]["socket_power"]["value"])])
-            except (KeyError, TypeError, ValueError, ZeroDivisionError, AttributeError):
-                pass
-        if select.select([fd], [], [], 0)[0] or d is None:
-            break
-    print(json.dumps({"bdf": bdf, "samples": samples}), flush=True)
-    return 0
+        got = os.read(fd, 64)
+        if not got:
+            return 0
+        if bdf is None:
+            bdf = {}
+            for g in smi_json("list") or []:
+                if isinstance(g, dict) and "gpu" in g:
+                    bdf[str(g["gpu"])] = str(g.get("bdf", "")).lower()
+        samples = []
+        ended = False
+        while True:
+            d = smi_json("metric", "-c", "-p")
+            for g in (d or {}).get("gpu_data", []) if isinstance(d, dict) else []:
+                try:
+                    clks = [v["clk"]["value"] for k, v in g["clock"].items()
+                            if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+                    samples.append([str(g["gpu"]), sum(clks) / len(clks),
+                                    float(g["power"]["socket_power"]["value"])])
+                except (KeyError, TypeError, ValueError, ZeroDivisionError, AttributeError):
+                    pass
+            if d is None:
+                ended = True
+                break
+            if select.select([fd], [], [], 0)[0]:
+                ended = not os.read(fd, 64)
+                break
+        print(json.dumps({"bdf": bdf, "samples": samples}), flush=True)
+        if ended:
+            return 0
 
 
 def start_sampler():
@@ -117,12 +129,25 @@ def tell(sampler, line):
         pass
 
 
-def clock_window(sampler, seconds, step, stream, flops, props, peak_tflops, label="bench"):
+def read_window(sampler, keep: bool, timeout: float = 60.0) -> str:
+    """The sampler's report of the window just stopped: with keep, one line
+    read while the child waits for the next window; else its whole output
+    once its input is closed (the child then exits)."""
+    if not keep:
+        return sampler.communicate(timeout=timeout)[0]
+    import select
+    if not select.select([sampler.stdout], [], [], timeout)[0]:
+        raise subprocess.TimeoutExpired("amd-smi sampler", timeout)
+    return sampler.stdout.readline()
+
+
+def clock_window(sampler, seconds, step, stream, flops, props, peak_tflops, label="bench", keep=False):
     """Back-to-back calls of step() for `seconds` while the sampler child
     polls amd-smi: the rate (flops per call over the event-timed window on
     `stream`), the engine clock and board power under that load, and the
     rate as a share of peak_tflops scaled to the median clock (peak_tflops
-    is quoted at 2.4 GHz).  None when amd-smi gave no samples."""
+    is quoted at 2.4 GHz).  None when amd-smi gave no samples.  With keep
+    the sampler stays up for another window."""
     import torch
 
     s0 = torch.cuda.Event(enable_timing=True)
@@ -142,8 +167,8 @@ def clock_window(sampler, seconds, step, stream, flops, props, peak_tflops, labe
     tell(sampler, "stop")
     torch.cuda.synchronize()
     try:
-        got = json.loads(sampler.communicate(timeout=60)[0].strip().splitlines()[-1])
-    except (ValueError, IndexError, subprocess.SubprocessError):
+        got = json.loads(read_window(sampler, keep).strip().splitlines()[-1])
+    except (ValueError, IndexError, OSError, subprocess.SubprocessError):
         log("%s: amd-smi gave no samples; no clock window" % label)
         return None
     mine = samples_of(got, props.pci_domain_id, props.pci_bus_id)

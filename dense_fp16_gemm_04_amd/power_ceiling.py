@@ -11,7 +11,9 @@ fragment reads, the global->LDS loads and the barrier of the real loop.  Each
 row runs back to back for --settle seconds, then for a --window of seconds
 while a child process samples the engine clock and board power with amd-smi
 (``clock.py``); the last row is the GEMM itself, the library's own plan on
-the workload, measured the same way.
+the workload, measured the same way.  The chip drifts over a run, so the
+rows run in --passes passes, alternately forward and backward, and each
+row reports the mean of its passes.
 
 The percentage of the peak at the clock is the share of cycles in which the
 matrix cores worked: every flop of a row is an MFMA's, and the peak at clock
@@ -75,16 +77,17 @@ def table(records) -> str:
     """Markdown table of the rows' records (dicts with name, what, tflops,
     sclk_mhz_median, power_w_mean, pct_of_peak_at_sclk)."""
     base = next((r["tflops"] for r in records if r["name"] == "mfma" and r.get("tflops")), None)
-    out = ["| row | what runs | TFLOP/s | % of the 2516.6 peak | engine MHz (median) | board W (mean) | "
+    out = ["| row | what runs | TFLOP/s | each pass | % of the 2516.6 peak | engine MHz (median) | board W (mean) | "
            "matrix cores busy (% of the peak at that clock) | vs MFMAs only |",
-           "|---|---|---|---|---|---|---|---|"]
+           "|---|---|---|---|---|---|---|---|---|"]
     for r in records:
         if r.get("tflops") is None:
-            out.append("| `%s` | %s | - | - | - | - | - | - |" % (r["name"], r["what"]))
+            out.append("| `%s` | %s | - | - | - | - | - | - | - |" % (r["name"], r["what"]))
             continue
         mhz = r.get("sclk_mhz_median")
-        out.append("| `%s` | %s | %.1f | %.1f%% | %s | %s | %s | %s |" % (
-            r["name"], r["what"], r["tflops"], 100 * r["tflops"] / PEAK_TFLOPS,
+        each = " / ".join("%.1f" % t for t in r.get("tflops_passes", [r["tflops"]]) if t is not None)
+        out.append("| `%s` | %s | %.1f | %s | %.1f%% | %s | %s | %s | %s |" % (
+            r["name"], r["what"], r["tflops"], each, 100 * r["tflops"] / PEAK_TFLOPS,
             "%.0f" % mhz if mhz else "-",
             "%.0f" % r["power_w_mean"] if r.get("power_w_mean") else "-",
             "%.1f%%" % r["pct_of_peak_at_sclk"] if r.get("pct_of_peak_at_sclk") else "-",
@@ -110,20 +113,48 @@ def timed_only(seconds, step, stream, flops):
     return {"seconds": seconds, "launches": n, "ms_per_launch": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
+def combine(name, what, passes) -> dict:
+    """One row's record from its passes: the means of the rate, the median
+    clock, the power and the busy share; each pass's rate kept."""
+    out = {"name": name, "what": what, "passes": passes,
+           "tflops_passes": [r.get("tflops") for r in passes]}
+    for key in ("tflops", "sclk_mhz_median", "power_w_mean", "pct_of_peak_at_sclk"):
+        vals = [r[key] for r in passes if r.get(key) is not None]
+        out[key] = sum(vals) / len(vals) if len(vals) == len(passes) else None
+    return out
+
+
+def order(n: int, passes: int) -> list:
+    """Row indices in run order: forward, then backward, and so on, so that a
+    drift linear in time weighs every row's mean alike."""
+    seq = []
+    for p in range(passes):
+        seq += list(range(n)) if p % 2 == 0 else list(range(n - 1, -1, -1))
+    return seq
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--settle", type=float, default=1.0, metavar="SECONDS")
     p.add_argument("--window", type=float, default=3.0, metavar="SECONDS")
+    p.add_argument("--passes", type=int, default=2,
+                   help="passes over the rows, alternately forward and backward (the rows' means are reported)")
     p.add_argument("--steps", type=int, default=512, help="probe steps (128 MFMAs per wave each) per launch")
     p.add_argument("--workload", default="square_8192")
     p.add_argument("--json", default="", help="also write the records to this file")
     args = p.parse_args(argv)
-    if args.steps < 1 or args.window <= 0 or args.settle < 0:
-        print("power_ceiling: --steps must be >= 1, --window > 0, --settle >= 0", file=sys.stderr)
+    if args.steps < 1 or args.window <= 0 or args.settle < 0 or args.passes < 1:
+        print("power_ceiling: --steps and --passes must be >= 1, --window > 0, --settle >= 0", file=sys.stderr)
         return 2
-    # one sampler per row, all started before this process touches the GPU
-    samplers = [clock.start_sampler() for _ in range(len(ROWS) + 1)]
+    # the sampler starts before this process touches the GPU, and serves every window
+    sampler = clock.start_sampler()
+    try:
+        return measure(args, sampler)
+    finally:
+        clock.stop_sampler(sampler)
 
+
+def measure(args, sampler) -> int:
     import torch
 
     from dense_fp16_gemm_04_amd import binding, workloads
@@ -145,8 +176,13 @@ def main(argv=None) -> int:
     grid = props.multi_processor_count
     sink = torch.empty(grid * 256, device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream()
+    a, b = workloads.workload_inputs(w)
+    A = torch.from_numpy(a).to(dev)
+    B = torch.from_numpy(b).to(dev)
+    C = torch.empty(w.M, w.N, device=dev, dtype=torch.float16)
+    kernel = binding.gemm_nt_f16_config_name(w.M, w.N, w.K)
 
-    def run_row(step, flops, sampler, label):
+    def run_row(step, flops, label):
         step()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -154,38 +190,39 @@ def main(argv=None) -> int:
             for _ in range(10):
                 step()
             torch.cuda.synchronize()
-        if sampler is not None:
+        if sampler is not None and sampler.poll() is None:
             rec = clock.clock_window(sampler, args.window, step, stream, flops, props, PEAK_TFLOPS,
-                                     label="power_ceiling: " + label)
+                                     label="power_ceiling: " + label, keep=True)
             if rec is not None:
                 return rec
-        return timed_only(args.window, step, stream, flops)
+        rec = timed_only(args.window, step, stream, flops)
+        print("power_ceiling: %s: %.1f TFLOP/s (no clock samples)" % (label, rec["tflops"]), file=sys.stderr,
+              flush=True)
+        return rec
 
-    records = []
-    for m, ((name, what), sampler) in enumerate(zip(ROWS, samplers)):
-        def step(m=m):
+    def probe_step(m, name):
+        def step():
             rc = lib.power_probe_launch(m, src.data_ptr(), src.numel() * 2, sink.data_ptr(), grid, args.steps,
                                         ctypes.c_void_p(stream.cuda_stream))
             if rc != 0:
                 raise RuntimeError("power_probe_launch(%s) returned hipError_t %d" % (name, rc))
-        flops = float(grid) * 4 * args.steps * 128 * MFMA_FLOP
-        records.append({"name": name, "what": what, **run_row(step, flops, sampler, name)})
-
-    a, b = workloads.workload_inputs(w)
-    A = torch.from_numpy(a).to(dev)
-    B = torch.from_numpy(b).to(dev)
-    C = torch.empty(w.M, w.N, device=dev, dtype=torch.float16)
-    kernel = binding.gemm_nt_f16_config_name(w.M, w.N, w.K)
+        return step
 
     def gemm():
         binding.gemm_nt_f16(A, B, C)
-    rec = run_row(gemm, 2.0 * w.M * w.N * w.K, samplers[-1], "gemm " + args.workload)
-    records.append({"name": "gemm", "what": "the GEMM on %s (%d x %d x %d), the library's plan: `%s`"
-                    % (w.name, w.M, w.N, w.K, kernel), **rec})
-    for s in samplers:
-        clock.stop_sampler(s)
+
+    probe_flops = float(grid) * 4 * args.steps * 128 * MFMA_FLOP
+    items = [(name, what, probe_step(m, name), probe_flops) for m, (name, what) in enumerate(ROWS)]
+    items.append(("gemm", "the GEMM on %s (%d x %d x %d), the library's plan: `%s`" % (w.name, w.M, w.N, w.K, kernel),
+                  gemm, 2.0 * w.M * w.N * w.K))
+    runs = [[] for _ in items]
+    for i in order(len(items), args.passes):
+        name, _, step, flops = items[i]
+        runs[i].append(run_row(step, flops, name))
+    records = [combine(name, what, runs[i]) for i, (name, what, _, _) in enumerate(items)]
     print(table(records))
-    print(json.dumps({"workload": w.name, "grid": grid, "steps": args.steps, "records": records}))
+    print(json.dumps({"workload": w.name, "grid": grid, "steps": args.steps, "passes": args.passes,
+                      "records": records}))
     if args.json:
         with open(args.json, "w") as f:
             json.dump(records, f, indent=1)

@@ -96,6 +96,31 @@ def test_clock_sampler_protocol(tmp_path, entry):
     assert bench.samples_of(got, 0, 0x99) == []
 
 
+def test_one_sampler_serves_window_after_window(tmp_path):
+    """After a window's report the sampler waits for the next start line;
+    read_window(keep=True) takes one report and leaves the child running."""
+    import time
+
+    script = tmp_path / "amdsmi_cli.py"
+    script.write_text(FAKE_SMI)
+    script.chmod(0o755)
+    (tmp_path / "amd-smi").symlink_to(script)
+    env = dict(__import__("os").environ, PATH="%s:%s" % (tmp_path, __import__("os").environ.get("PATH", "")))
+    proc = subprocess.Popen(SAMPLER_COMMANDS["clock"], stdin=subprocess.PIPE, stdout=subprocess.PIPE, text=True,
+                            env=env)
+    reports = []
+    for _ in range(2):
+        clock.tell(proc, "start")
+        time.sleep(0.5)
+        clock.tell(proc, "stop")
+        reports.append(json.loads(clock.read_window(proc, keep=True, timeout=60)))
+        assert proc.poll() is None
+    clock.stop_sampler(proc)
+    assert proc.returncode == 0
+    for got in reports:
+        assert got["samples"] and clock.samples_of(got, 0, 0x75)[0] == (1510.0, 1300.0)
+
+
 @pytest.mark.parametrize("entry", sorted(SAMPLER_COMMANDS))
 def test_clock_sampler_without_a_start_line_exits(entry):
     proc = subprocess.run(SAMPLER_COMMANDS[entry], input="", stdout=subprocess.PIPE, text=True, timeout=60)

@@ -92,23 +92,41 @@ def test_full_mix_issues_what_the_default_k_loop_issues(tmp_path):
     assert not [k for k in wide[0] if k.startswith(("v_", "ds_", "buffer_")) and not k.startswith("v_mfma")], wide
 
 
+def test_rows_run_forward_then_backward():
+    assert power_ceiling.order(3, 1) == [0, 1, 2]
+    assert power_ceiling.order(3, 2) == [0, 1, 2, 2, 1, 0]
+    assert power_ceiling.order(2, 3) == [0, 1, 1, 0, 0, 1]
+
+
+def test_a_row_reports_the_mean_of_its_passes():
+    passes = [{"tflops": 1500.0, "sclk_mhz_median": 1650.0, "power_w_mean": 1300.0, "pct_of_peak_at_sclk": 89.0},
+              {"tflops": 1540.0, "sclk_mhz_median": 1690.0, "power_w_mean": 1310.0, "pct_of_peak_at_sclk": 90.0}]
+    r = power_ceiling.combine("k_loop_mix", "all", passes)
+    assert r["tflops"] == 1520.0 and r["sclk_mhz_median"] == 1670.0 and r["power_w_mean"] == 1305.0
+    assert r["pct_of_peak_at_sclk"] == 89.5 and r["tflops_passes"] == [1500.0, 1540.0]
+    # a pass without clock samples leaves the clock columns empty, the rate not
+    r = power_ceiling.combine("k_loop_mix", "all", [passes[0], {"tflops": 1540.0}])
+    assert r["tflops"] == 1520.0 and r["sclk_mhz_median"] is None
+
+
 def test_table_reads_against_mfma_only():
-    recs = [{"name": "mfma_zero_data", "what": "zeros", "tflops": 2400.0, "sclk_mhz_median": 2390.0,
-             "power_w_mean": 700.0, "pct_of_peak_at_sclk": 96.0},
+    recs = [{"name": "mfma_zero_data", "what": "zeros", "tflops": 2400.0, "tflops_passes": [2390.0, 2410.0],
+             "sclk_mhz_median": 2390.0, "power_w_mean": 700.0, "pct_of_peak_at_sclk": 96.0},
             {"name": "mfma", "what": "Gaussian", "tflops": 1800.0, "sclk_mhz_median": 1870.0,
              "power_w_mean": 1330.0, "pct_of_peak_at_sclk": 94.0},
             {"name": "k_loop_mix", "what": "all", "tflops": 1500.0},
             {"name": "gemm", "what": "the GEMM"}]
     t = power_ceiling.table(recs).splitlines()
     assert len(t) == 2 + len(recs)
-    assert "| 2400.0 | 95.4% | 2390 | 700 | 96.0% | +33.3% |" in t[2]
-    assert "| +0.0% |" in t[3]
-    assert "| 1500.0 | 59.6% | - | - | - | -16.7% |" in t[4]
-    assert t[5].endswith("| - | - | - | - | - | - |")
+    assert t[0].count("|") == t[2].count("|") == 10
+    assert "| 2400.0 | 2390.0 / 2410.0 | 95.4% | 2390 | 700 | 96.0% | +33.3% |" in t[2]
+    assert "| 1800.0 | 1800.0 | 71.5% |" in t[3] and t[3].endswith("| +0.0% |")
+    assert "| 1500.0 | 1500.0 | 59.6% | - | - | - | -16.7% |" in t[4]
+    assert t[5].endswith("| the GEMM | - | - | - | - | - | - | - |")
 
 
 def test_driver_rejects_bad_arguments_before_starting_anything(capsys):
-    for bad in (["--steps", "0"], ["--window", "0"], ["--settle", "-1"]):
+    for bad in (["--steps", "0"], ["--window", "0"], ["--settle", "-1"], ["--passes", "0"]):
         assert power_ceiling.main(bad) == 2, bad
     assert "power_ceiling:" in capsys.readouterr().err
 
