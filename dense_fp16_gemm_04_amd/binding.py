@@ -102,22 +102,52 @@ def _check(a, b, out):
         raise TypeError("a and b must be float16")
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
         raise ValueError("need a [M, K] and b [N, K], got %s and %s" % (tuple(a.shape), tuple(b.shape)))
-    if not a.is_cuda or a.device != b.device:
+    index = a.get_device()  # -1 for host memory
+    if not a.is_cuda or b.get_device() != index:
         raise ValueError("a and b must be on the same GPU")
     if not (a.is_contiguous() and b.is_contiguous()):
         raise ValueError("a and b must be contiguous (row-major, K innermost)")
     M, N = a.shape[0], b.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=a.device)
-    elif (out.dtype != torch.float16 or tuple(out.shape) != (M, N) or out.device != a.device
-          or not out.is_contiguous()):
+    elif (not isinstance(out, torch.Tensor) or out.dtype != torch.float16 or out.dim() != 2
+          or out.shape[0] != M or out.shape[1] != N or out.get_device() != index or not out.is_contiguous()):
         raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
     return out
 
 
-def _stream(a):
+_raw_stream_of = None
+
+
+def _stream(index: int) -> int:
+    """The HIP stream handle of the current stream of device `index` (torch's
+    own accessor for it; the public Stream object where that is missing)."""
+    global _raw_stream_of
+    if _raw_stream_of is None:
+        import torch
+        _raw_stream_of = getattr(torch._C, "_cuda_getCurrentRawStream", None) or (
+            lambda i: torch.cuda.current_stream(i).cuda_stream)
+    return _raw_stream_of(index)
+
+
+def _launch(name, a, b, out, *extra):
+    """Check the tensors, then call entry point `name` on a's device and its
+    current stream; the library plans for the current device, so another
+    device is made current for the call."""
     import torch
-    return ctypes.c_void_p(torch.cuda.current_stream(a.device).cuda_stream)
+    out = _check(a, b, out)
+    M, K = a.shape
+    N = b.shape[0]
+    fn = getattr(load(), name)
+    index = a.get_device()
+    if index == torch.cuda.current_device():
+        rc = fn(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, *extra, _stream(index))
+    else:
+        with torch.cuda.device(index):
+            rc = fn(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, *extra, _stream(index))
+    if rc != 0:
+        raise GemmError(name, rc)
+    return out
 
 
 def gemm_nt_f16(a, b, out=None):
@@ -125,26 +155,9 @@ def gemm_nt_f16(a, b, out=None):
 
     Enqueued on the current stream of a's device; returns ``out``.
     """
-    import torch
-    out = _check(a, b, out)
-    M, K = a.shape
-    N = b.shape[0]
-    with torch.cuda.device(a.device):  # the library plans for the current device
-        rc = load().gemm_nt_f16(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, _stream(a))
-    if rc != 0:
-        raise GemmError("gemm_nt_f16", rc)
-    return out
+    return _launch("gemm_nt_f16", a, b, out)
 
 
 def gemm_nt_f16_ex(a, b, out=None, variant: int = -1):
     """``gemm_nt_f16`` with an explicit kernel variant (index into ``variants()``)."""
-    import torch
-    out = _check(a, b, out)
-    M, K = a.shape
-    N = b.shape[0]
-    with torch.cuda.device(a.device):
-        rc = load().gemm_nt_f16_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, int(variant),
-                                   _stream(a))
-    if rc != 0:
-        raise GemmError("gemm_nt_f16_ex", rc)
-    return out
+    return _launch("gemm_nt_f16_ex", a, b, out, int(variant))
