@@ -47,5 +47,6 @@ def pytest_terminal_summary(terminalreporter):
             r["bit_equal_to_rne_c64"], r["rne_floor_mean"], r["rne_floor_max"]))
     path = os.environ.get("GEMM_ERROR_REPORT")
     if path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
         with open(path, "w") as f:
             json.dump(_errstats.RECORDS, f, indent=1)

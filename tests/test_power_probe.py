@@ -1,7 +1,7 @@
 """The power probe: its modes and argument checks, the instruction mix of its
 loops against the default kernel's K loop (read from both libraries' gfx950
-code objects), and the table of the driver (no GPU); one short launch of
-every mode on the GPU."""
+code objects), and power_ceiling.py's run order and table (no GPU); one
+short launch of every mode on the GPU."""
 from __future__ import annotations
 
 import ctypes
@@ -23,7 +23,7 @@ def lib():
     return power_ceiling.load_probe()
 
 
-def test_modes_match_the_driver_rows(lib):
+def test_modes_match_the_rows_of_power_ceiling(lib):
     assert power_ceiling.probe_modes(lib) == [n for n, _ in power_ceiling.ROWS]
     assert lib.power_probe_mode_name(-1) is None
     assert lib.power_probe_mode_name(len(power_ceiling.ROWS)) is None
@@ -125,7 +125,7 @@ def test_table_reads_against_mfma_only():
     assert t[5].endswith("| the GEMM | - | - | - | - | - | - | - |")
 
 
-def test_driver_rejects_bad_arguments_before_starting_anything(capsys):
+def test_power_ceiling_rejects_bad_arguments_before_starting_anything(capsys):
     for bad in (["--steps", "0"], ["--window", "0"], ["--settle", "-1"], ["--passes", "0"]):
         assert power_ceiling.main(bad) == 2, bad
     assert "power_ceiling:" in capsys.readouterr().err
