@@ -587,3 +587,33 @@ def test_non_default_stream():
         c = binding.gemm_nt_f16(ta, tb)
     s.synchronize()
     assert_close(c.cpu().numpy(), c64, c16, 264, "side stream")
+
+
+def test_binding_makes_a_device_current_when_another_is(monkeypatch):
+    """The binding calls the library with a's device current: when torch
+    reports another current device it enters a's device for the call.  On
+    one GPU the other device is simulated; the result is bit-identical to
+    the ordinary call and to the oracle."""
+    torch = _torch()
+    a, b = workloads.gaussian(300, 200, 136, seed=47)
+    c64, c16 = oracle.gemm_nt(a, b)
+    ta = torch.from_numpy(a).to(dev())
+    tb = torch.from_numpy(b).to(dev())
+    ref = binding.gemm_nt_f16(ta, tb)
+    entered = []
+    real_device = torch.cuda.device
+
+    class Tracking(real_device):
+        def __enter__(self):
+            entered.append(self.idx)
+            return super().__enter__()
+
+    # patched for the binding's call only: nothing else may see the simulated device
+    with monkeypatch.context() as m:
+        m.setattr(torch.cuda, "current_device", lambda: ta.get_device() + 1)
+        m.setattr(torch.cuda, "device", Tracking)
+        c = binding.gemm_nt_f16(ta, tb)
+    torch.cuda.synchronize()
+    assert entered == [ta.get_device()]
+    assert torch.equal(c.view(torch.int16), ref.view(torch.int16))
+    assert_close(c.cpu().numpy(), c64, c16, 136, "device switch")
